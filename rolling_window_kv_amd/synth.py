@@ -1,0 +1,76 @@
+"""Seeded synthetic inputs (q, k_new, v_new) for the rolling-KV workloads.
+
+This module only draws random numbers; it holds none of the method's
+arithmetic, so both the GPU path's tests/benchmark and the CPU oracle consume
+exactly the same bfloat16 values from it.
+
+Every (layer, stream) pair owns an independent NumPy generator seeded with
+``[seed, layer, stream]``, so any pair's inputs can be regenerated on its own.
+A step pool of ``period`` entries is drawn per pair; step i uses entry
+``i % period`` (the benchmark cycles a device-resident pool; parity runs use a
+period at least as long as the run so no entry repeats).
+
+Values are N(0, 1) in float32, optionally with element-wise outliers
+(probability ``outlier_frac``, scaled by ``outlier_scale``), then rounded to
+bfloat16 by torch (round to nearest even).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def _block(seed, layer, stream, shape, outlier_frac=0.0, outlier_scale=8.0):
+    rng = np.random.default_rng([int(seed), int(layer), int(stream)])
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if outlier_frac > 0.0:
+        hit = rng.random(shape, dtype=np.float32) < outlier_frac
+        x = np.where(hit, x * np.float32(outlier_scale), x)
+    return x
+
+
+def decoder_pair(seed, layer, stream, period, hq, hkv, d, outlier_frac=0.0):
+    """One (layer, stream): q [P, Hq, d], k [P, Hkv, d], v [P, Hkv, d] (bf16, CPU)."""
+    x = _block(seed, layer, stream, (period, hq + 2 * hkv, d), outlier_frac)
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    return t[:, :hq].contiguous(), t[:, hq:hq + hkv].contiguous(), t[:, hq + hkv:].contiguous()
+
+
+def decoder_pool(seed, layers, streams, period, hq, hkv, d, outlier_frac=0.0):
+    """All pairs: q [P, L, S, Hq, d], k/v [P, L, S, Hkv, d] (bf16, CPU).
+
+    ``layers``/``streams`` are counts; pair (l, s) equals
+    ``decoder_pair(seed, l, s, ...)``.
+    """
+    q = torch.empty((period, layers, streams, hq, d), dtype=torch.bfloat16)
+    k = torch.empty((period, layers, streams, hkv, d), dtype=torch.bfloat16)
+    v = torch.empty((period, layers, streams, hkv, d), dtype=torch.bfloat16)
+    for l in range(layers):
+        for s in range(streams):
+            q[:, l, s], k[:, l, s], v[:, l, s] = decoder_pair(
+                seed, l, s, period, hq, hkv, d, outlier_frac)
+    return q, k, v
+
+
+def encoder_pair(seed, layer, stream, period, frames, heads, d):
+    """One (layer, stream): q, k, v each [P, F, H, d] (bf16, CPU)."""
+    x = _block(seed, layer, stream, (period, 3, frames, heads, d))
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    return t[:, 0].contiguous(), t[:, 1].contiguous(), t[:, 2].contiguous()
+
+
+def encoder_pool(seed, layers, streams, period, frames, heads, d):
+    """All pairs: q, k, v each [P, L, S, F, H, d] (bf16, CPU)."""
+    shape = (period, layers, streams, frames, heads, d)
+    q, k, v = (torch.empty(shape, dtype=torch.bfloat16) for _ in range(3))
+    for l in range(layers):
+        for s in range(streams):
+            q[:, l, s], k[:, l, s], v[:, l, s] = encoder_pair(
+                seed, l, s, period, frames, heads, d)
+    return q, k, v
+
+
+def start_offsets(seed, streams, high):
+    """Per-stream start offsets, uniform integers in [0, high]."""
+    rng = np.random.default_rng([int(seed), 0x5EED])
+    return rng.integers(0, high + 1, size=streams).astype(np.int64)
