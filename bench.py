@@ -1,0 +1,367 @@
+"""Throughput of the rolling-window KV decode path on one MI355X.
+
+Default workload: 36 layers x 64 streams, 16 query / 2 KV heads, head_dim 128,
+bf16 rings of W = 375 positions (30 s at the 80 ms clock), base re-based in
+chunks of 25 positions.  A step is one clock step of every stream through the
+whole path: rkv_advance (plan) + rkv_decode_step (re-base, append and GQA
+decode attention for all 36 layers in one pass).  Inputs are synthetic
+N(0, 1) bf16 tensors already resident on the GPU (a pool of steps cycled).
+
+Prints one JSON line: stream-layer decode steps per second (value), the
+roofline of the dominant kernel (algorithmic bytes per launch over the
+launch's average duration, timed with HIP events on the launch stream), and
+the CPU oracle timed on a bounded sample on the host cores.
+
+Other workloads (--config): 1 = one layer x one stream, re-base every step
+(compensated); 3 = 256 streams of mixed windows 375/250/188 with start
+offsets and 1 % x8 outliers; 4 = 26 x 16 streams, window 8192, logical-offset
+compaction; 5 = encoder chunks, 32 x 128 streams, 20 heads x 64, 4 frames per
+step over a 750-frame window.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBPS = 8000.0
+
+METRIC = "stream-layer decode steps/sec + achieved HBM GB/s (% of peak), W=375 window"
+
+CONFIGS = {
+    1: dict(name="1 layer x 1 stream, 16q/2kv d128 bf16, W=375, re-base every step "
+                 "(compensated), 1000 steps",
+            mode="rebase", L=1, S=1, W=375, dc=1, comp=True, period=1000, steps=1000, warmup=0),
+    2: dict(name="36 layers x 64 streams, 16q/2kv d128 bf16, W=375 rings, re-base chunk 25",
+            mode="rebase", L=36, S=64, W=375, dc=25, comp=False, period=64, steps=2000, warmup=100),
+    3: dict(name="36 layers x 256 streams, W mix 375/250/188 (86/85/85), re-base chunk 25, "
+                 "start offsets U[0,5000], 1% x8 outliers",
+            mode="rebase", L=36, S=256, W=(375, 250, 188), dc=25, comp=False, period=16,
+            steps=600, warmup=50, outlier=0.01, offsets=5000),
+    4: dict(name="26 layers x 16 streams, 16q/2kv d128 bf16, window 8192, capacity 9216, "
+                 "logical-offset compaction",
+            mode="compact", L=26, S=16, W=8192, cap=9216, period=16, steps=1024, warmup=16),
+    5: dict(name="encoder chunks: 32 layers x 128 streams, 20 heads x d64 bf16, F=4 frames "
+                 "per step, 750-frame window (ring 754)",
+            mode="enc", L=32, S=128, H=20, d=64, F=4, W=750, period=4, steps=400, warmup=20),
+}
+
+
+def bytes_per_sl_step(c):
+    """Algorithmic bytes of one (stream, layer) step: every byte the step must
+    move at least once (bf16 = 2 bytes)."""
+    if c["mode"] == "rebase":
+        Hq, Hkv, d = 16, 2, 128
+        Ws = c["W"] if isinstance(c["W"], tuple) else (c["W"],)
+        mix = [86, 85, 85] if len(Ws) == 3 else [1]
+        total = 0.0
+        for W, n in zip(Ws, mix):
+            row = Hkv * d * 2                                   # one K (or V) row, all KV heads
+            b = W * 2 * row                                     # K and V window read
+            b += 2 * Hq * d * 2                                 # q in, out
+            b += 2 * row + 2 * row                              # k_new/v_new in, appended K/V
+            b += (W - 1) * row / c["dc"]                        # re-based K written
+            if c.get("comp"):
+                b += 2 * (W - 1) * row / c["dc"] + row          # residual read + written, appended
+            total += b * n
+        return total / sum(mix)
+    if c["mode"] == "compact":
+        Hq, Hkv, d = 16, 2, 128
+        row = Hkv * d * 2
+        E = c["cap"] - c["W"]
+        avg_len = (c["W"] + 1 + c["cap"]) / 2.0
+        return (avg_len * 2 * row + 2 * Hq * d * 2 + 4 * row
+                + 2 * 2 * c["W"] * row / E)                     # compaction read + write, amortised
+    H, d, F, W = c["H"], c["d"], c["F"], c["W"]
+    row = H * d * 2
+    return W * 2 * row + 2 * F * row + 2 * F * row + 2 * F * row  # cached read, q/out, new in, append
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for name in ("attn.hip", "rkv_device.h", "rkv_internal.h"):
+        with open(os.path.join(ROOT, "rolling_window_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    the summary is missing or was taken from a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(f"{kernel}@{workload}")
+    if not ent or ent.get("kernel_src_digest") != kernel_source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+
+def _oracle_worker(args):
+    seed, stream, c, fill, steps, budget = args
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        from oracle import schedule as sch
+        from oracle import storage as stg
+        from rolling_window_kv_amd import synth
+        W = c["W"][0] if isinstance(c["W"], tuple) else c["W"]
+        n = fill + steps
+        P = c["period"]                       # the same input pool the GPU run cycles
+        if c["mode"] == "enc":
+            q, k, v = synth.encoder_pair(seed, 0, stream, P, c["F"], c["H"], c["d"])
+            q, k, v = (x.double().numpy()[np.arange(n) % P] for x in (q, k, v))
+            ring = stg.EncoderRing(c["H"], c["d"], W, c["F"], 1e6)
+        else:
+            q, k, v = synth.decoder_pair(seed, 0, stream, P, 16, 2, 128, c.get("outlier", 0.0))
+            q, k, v = (x.double().numpy()[np.arange(n) % P] for x in (q, k, v))
+            if c["mode"] == "compact":
+                ring = stg.CompactBuffer(16, 2, 128, W, c["cap"], 1e6)
+            else:
+                ring = stg.RebaseRing(16, 2, 128, W, c["dc"], 1e6, compensated=c.get("comp", False))
+        if c["mode"] == "compact":
+            # Fill the first `fill` rows with the oracle's own append (vectorised)
+            # and its schedule, instead of `fill` full attention steps.
+            for _ in range(fill):
+                sch.step(sch.MODE_COMPACT, ring.state)
+            hi, _ = stg.append_k(k[:fill], np.arange(fill)[:, None], 1e6)
+            ring.k[:, :fill] = hi.transpose(1, 0, 2)
+            ring.v[:, :fill] = v[:fill].transpose(1, 0, 2)
+        else:
+            for t in range(fill):
+                ring.step(q[t], k[t], v[t])
+        t0 = time.perf_counter()
+        done = 0
+        for t in range(fill, n):
+            ring.step(q[t], k[t], v[t])
+            done += 1
+            if time.perf_counter() - t0 > budget:
+                break
+        return done, time.perf_counter() - t0
+
+
+def cpu_baseline(c, seed, budget_s=15.0):
+    """Storage-faithful oracle (plan, re-base, append and attention per step,
+    float64 NumPy) on a bounded sample: one layer of several streams, each
+    filled to a full window untimed, then timed for a fixed number of steps."""
+    import multiprocessing as mp
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    workers = max(1, min(16, cores, c["S"]))
+    W = c["W"][0] if isinstance(c["W"], tuple) else c["W"]
+    if c["mode"] == "compact":
+        fill = (W + c["cap"]) // 2   # mid-way between two compactions
+    elif c["mode"] == "enc":
+        fill = (W + c["F"] - 1) // c["F"] + 1
+    else:
+        fill = W
+    max_steps = 200000
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        res = pool.map(_oracle_worker,
+                       [(seed, s, c, fill, max_steps, budget_s) for s in range(workers)])
+    wall = time.perf_counter() - t0
+    total = sum(r[0] for r in res)
+    timed = max(r[1] for r in res)
+    return {"value": total / timed, "unit": "stream-layer steps/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"storage-faithful float64 oracle, 1 layer x {workers} streams, "
+                      f"window pre-filled ({fill} steps untimed), then timed steps for "
+                      f"{budget_s:g} s per stream ({total} steps in all), one process per "
+                      f"stream ({wall:.1f} s wall incl. fill)"}
+
+
+# ---------------------------------------------------------------------------
+# GPU run
+# ---------------------------------------------------------------------------
+
+def build_inputs(c, seed, dev):
+    import torch
+    from rolling_window_kv_amd import synth
+    P = c["period"]
+    if c["mode"] == "enc":
+        q, k, v = synth.encoder_pool(seed, c["L"], c["S"], P, c["F"], c["H"], c["d"])
+    else:
+        q, k, v = synth.decoder_pool(seed, c["L"], c["S"], P, 16, 2, 128, c.get("outlier", 0.0))
+    return q.to(dev), k.to(dev), v.to(dev)
+
+
+def run_gpu(c, args):
+    import torch
+    from rolling_window_kv_amd import rkv
+    rkv.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    seed = 1000 + args.config
+    L, S = c["L"], c["S"]
+    t_setup = time.perf_counter()
+    q, k, v = build_inputs(c, seed, dev)
+    if c["mode"] == "rebase":
+        flags = rkv.RKV_F_COMPENSATED if c.get("comp") else 0
+        cfg = rkv.make_cfg(S, L, rebase_chunk=c["dc"], flags=flags)
+        if isinstance(c["W"], tuple):
+            counts = [86, 85, 85]
+            windows = np.repeat(np.array(c["W"], np.int32), counts)
+            from rolling_window_kv_amd import synth
+            t0 = synth.start_offsets(seed, S, c["offsets"])
+            origins = np.maximum(0, t0 - windows).astype(np.int64)
+        else:
+            windows = np.full(S, c["W"], np.int32)
+            origins = np.zeros(S, np.int64)
+        slots = int(windows.max())
+        cache = rkv.Cache(cfg, slots, windows, windows, origins, device=dev, zero=False)
+        prefill = slots
+    elif c["mode"] == "compact":
+        cfg = rkv.make_cfg(S, L, mode=rkv.RKV_MODE_COMPACT)
+        cache = rkv.Cache(cfg, c["cap"], c["W"], c["cap"], 0, device=dev, zero=False)
+        prefill = c["cap"]
+    else:
+        cfg = rkv.make_cfg(S, L, num_q_heads=c["H"], num_kv_heads=c["H"], head_dim=c["d"],
+                           mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=c["F"])
+        cap = c["W"] + c["F"]
+        cache = rkv.Cache(cfg, cap, c["W"], cap, 0, device=dev, zero=False)
+        prefill = (cap + c["F"] - 1) // c["F"]
+    out = torch.empty(q.shape[1:], dtype=torch.bfloat16, device=dev)
+    P = q.shape[0]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    ws = cache.workspace
+    separate = args.path == "separate"
+
+    def step(i, ev=None):
+        j = i % P
+        rkv.rkv_advance(cfg, cache.state, cache.plan, sp)
+        if c["mode"] == "compact":
+            rkv.rkv_compact(cfg, cache.plan, cache.kv, sp)
+        if ev is not None:
+            ev[0].record(stream)
+        if c["mode"] == "enc":
+            rkv.rkv_encoder_chunk_attn(cfg, cache.plan, cache.kv, q[j], k[j], v[j], out, ws, sp)
+        elif separate:
+            if c["mode"] == "rebase":
+                rkv.rkv_roll_rebase(cfg, cache.plan, cache.kv, sp)
+            rkv.rkv_append(cfg, cache.plan, cache.kv, k[j], v[j], sp)
+            rkv.rkv_decode_attn(cfg, cache.plan, cache.kv, q[j], out, ws, sp)
+        else:
+            rkv.rkv_decode_step(cfg, cache.plan, cache.kv, q[j], k[j], v[j], out, ws, sp)
+        if ev is not None:
+            ev[1].record(stream)
+
+    i = 0
+    for _ in range(prefill):          # fill every window (untimed set-up)
+        step(i)
+        i += 1
+    for _ in range(args.warmup):
+        step(i)
+        i += 1
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for n in range(K):
+        step(i, evs[n] if args.kernel_events else None)
+        i += 1
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed_ms = start.elapsed_time(end)
+    kernel_ms = (float(np.mean([a.elapsed_time(b) for a, b in evs]))
+                 if args.kernel_events else None)
+    return dict(cfg=cfg, elapsed_ms=elapsed_ms, kernel_ms=kernel_ms, wall_s=wall,
+                setup_s=setup_s, prefill=prefill)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS))
+    ap.add_argument("--path", choices=("fused", "separate"), default="fused",
+                    help="fused: rkv_decode_step; separate: rkv_roll_rebase + rkv_append + "
+                         "rkv_decode_attn")
+    ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
+    ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: streams are independent, so N GPUs would each "
+              "run the same per-GPU workload on their own streams with no communication; "
+              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    c = dict(CONFIGS[args.config])
+    args.steps = c["steps"] if args.steps is None else args.steps
+    args.warmup = c["warmup"] if args.warmup is None else args.warmup
+
+    r = run_gpu(c, args)
+    L, S, K = c["L"], c["S"], args.steps
+    secs = r["elapsed_ms"] / 1e3
+    sl_steps = L * S * K / secs
+    b_sl = bytes_per_sl_step(c)
+    step_gbps = b_sl * L * S * K / secs / 1e9
+    kernel = {"rebase": "attn_kernel<128,4,decode_fused>",
+              "compact": "attn_kernel<128,4,decode_fused>",
+              "enc": "attn_kernel<64,4,encoder_fused>"}[c["mode"]]
+    if args.path == "separate" and c["mode"] != "enc":
+        kernel = "rebase+append+attn_kernel<128,4,decode_read>"
+    roofline = None
+    if r["kernel_ms"]:
+        per_launch = b_sl * L * S
+        achieved = per_launch / (r["kernel_ms"] / 1e3) / 1e9
+        traffic = load_traffic(kernel, f"config{args.config}")
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                    "traffic": traffic, "kernel": kernel,
+                    "kernel_ms": round(r["kernel_ms"], 5),
+                    "alg_bytes_per_launch": per_launch}
+    res = {
+        "metric": METRIC,
+        "value": round(sl_steps, 1),
+        "unit": "stream-layer steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["elapsed_ms"] / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": c["name"], "layers": L, "streams": S,
+                   "path": args.path, "alg_bytes_per_stream_layer_step": b_sl},
+        "achieved_GBps_step": round(step_gbps, 1),
+        "hbm_frac_step": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "clock_steps_per_s": round(K / secs, 1),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if args.cpu:
+        res["cpu_baseline"] = cpu_baseline(c, 1000 + args.config, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,246 @@
+/*
+ * rkv.h -- rolling-window KV cache for streaming decode on AMD gfx950 (C ABI).
+ *
+ * The library computes one clock step of the streaming decoder's attention
+ * over a bounded KV cache, for a batch of independent streams and a range of
+ * layers, entirely in hand-written HIP kernels.  The three cache disciplines
+ * follow the pages this library implements:
+ *
+ *   RKV_MODE_REBASE  -- "Audio8 ASR Infinite" explainer (m.lsln.cn), section
+ *       "Rolling KV Cache 三步拆解": a fixed ~30 s window (W positions), the
+ *       oldest token pushed out per step, and exact RoPE re-basing: retained K
+ *       are rotated in place by R(-D) when the position base moves by D, so
+ *       stored positions stay inside the window.  Also the model card
+ *       (Edge0/Audio8-ASR-Infinite), "使用 vLLM 进行全天候推理".
+ *   RKV_MODE_COMPACT -- voxtral.c rolling-KV explainer (kwkr.cn), section 二:
+ *       the buffer grows to its capacity, then the newest W rows move to row 0
+ *       and the dropped count is added to kv_pos_offset; the rotary position
+ *       of a row is kv_pos_offset + its physical index, and K is never
+ *       rewritten.
+ *   RKV_MODE_ENC_CHUNK -- same explainer, section 三: the encoder appends a
+ *       chunk of F frames per step and attends to a 750-frame window of cached
+ *       K/V; here the window is a ring of W + F slots at logical positions.
+ *
+ * Conventions
+ *   - Every entry point returns 0 (RKV_OK) or a negative rkv_status.  All
+ *     arguments are validated on the host before any HIP call, so errors are
+ *     reported without touching a device.  No exception or abort crosses the
+ *     ABI.
+ *   - Device pointers are plain HIP device addresses; the caller allocates
+ *     and frees every buffer (rings, state, plan, inputs, outputs, workspace).
+ *     The library allocates no memory and keeps no global state besides the
+ *     thread-local last HIP error, so calls on different HIP streams with
+ *     disjoint buffers may run concurrently.
+ *   - Calls are asynchronous on the given hipStream_t (passed as void*; NULL
+ *     is the default stream).  Calls that share buffers must be ordered by
+ *     the caller (one stream does that).
+ *   - Element type of K, V, q, k_new, v_new is bfloat16 (raw 16-bit patterns).
+ *     Output is bfloat16, or float32 with RKV_F_OUT_F32.
+ *   - Rotary embedding: theta_i = rope_base^(-2i/d), i < d/2; element i pairs
+ *     with element i + d/2 (half-split).  Angles, their cosines/sines and every
+ *     rotation of a stored K are float64, and the stored bfloat16 is the
+ *     correctly rounded (nearest, ties to even) value of the float64 result.
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RKV_VERSION 1
+#define RKV_MAX_HEAD_DIM 128
+#define RKV_MAX_NEW_ROWS 8   /* frames per encoder chunk */
+#define RKV_MAX_GROUP 8      /* query vectors sharing one KV head */
+
+typedef enum rkv_status {
+  RKV_OK = 0,
+  RKV_EINVAL = -1,       /* null pointer, non-positive size, inconsistent sizes */
+  RKV_EUNSUPPORTED = -2, /* head_dim not 64/128, group > 8, F > 8, unknown mode/flag */
+  RKV_EALIGN = -3,       /* pointer not 16-byte aligned or stride not a multiple of 8 elements */
+  RKV_ESTATE = -4,       /* per-stream window/capacity/origin inconsistent with the mode */
+  RKV_EHIP = -5,         /* a HIP launch failed; see rkv_last_hip_error() */
+  RKV_ESPACE = -6        /* workspace smaller than rkv_workspace_bytes() */
+} rkv_status;
+
+typedef enum rkv_mode {
+  RKV_MODE_REBASE = 0,
+  RKV_MODE_COMPACT = 1,
+  RKV_MODE_ENC_CHUNK = 2
+} rkv_mode;
+
+enum {
+  /* REBASE mode: keep the bfloat16 rounding residual of every K in kv->k_lo
+   * and re-base the pair hi + lo, so repeated re-bases do not accumulate
+   * rounding (needed when the base moves every step).  Attention reads hi. */
+  RKV_F_COMPENSATED = 1u << 0,
+  /* write attention output as float32 instead of bfloat16 */
+  RKV_F_OUT_F32 = 1u << 1
+};
+
+/* Problem description, shared by every call of a step (host memory). */
+typedef struct rkv_cfg {
+  int32_t num_streams;   /* S >= 1 */
+  int32_t num_layers;    /* L >= 1 layers handled by one call */
+  int32_t num_q_heads;   /* Hq; ENC_CHUNK: heads H (multi-head, Hq == Hkv) */
+  int32_t num_kv_heads;  /* Hkv; Hq / Hkv <= 8 */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t mode;          /* rkv_mode */
+  int32_t rebase_chunk;  /* REBASE: the base moves in multiples of this (>= 1) */
+  int32_t new_rows;      /* rows appended per step: 1, or F (1..8) for ENC_CHUNK */
+  uint32_t flags;        /* RKV_F_* */
+  int32_t num_splits;    /* key-range splits per (layer, stream, head); 0 = library choice */
+  double rope_base;      /* > 0, e.g. 1e6 */
+  float softmax_scale;   /* 0 = 1/sqrt(d) */
+  int32_t reserved;
+} rkv_cfg;
+
+/* Per-stream cache state (device memory, S entries, 48 bytes each).
+ * Built by rkv_state_init_host and copied to the device by the caller;
+ * afterwards only rkv_advance writes it. */
+typedef struct rkv_stream_state {
+  int64_t t;          /* REBASE/COMPACT: step of the last appended token;
+                         ENC_CHUNK: position of the last appended frame; origin-1 at start */
+  int64_t origin;     /* first position of the stream */
+  int64_t pos_offset; /* REBASE: base b; COMPACT: kv_pos_offset; ENC_CHUNK: origin */
+  int32_t len;        /* valid rows */
+  int32_t window;     /* W */
+  int32_t cap;        /* ring slots used by this stream (<= kv->slots) */
+  int32_t reserved[3];
+} rkv_stream_state;
+
+/* Per-stream plan of the current step (device memory, S entries), written by
+ * rkv_advance and read by every other call of the step. */
+typedef struct rkv_step_plan {
+  int64_t t;            /* step (frame position of the last new frame for ENC_CHUNK) */
+  int64_t pos;          /* rotary position of the first new row: t - base (REBASE),
+                           kv_pos_offset + slot (COMPACT), frame position (ENC_CHUNK) */
+  int64_t pos_offset;   /* base / kv_pos_offset / origin after this step */
+  int64_t first_pos;    /* oldest position the new row(s) attend to */
+  int64_t evict_pos;    /* REBASE: position pushed out; COMPACT: first dropped; -1 none */
+  int32_t slot;         /* physical slot of the first new row */
+  int32_t n_valid;      /* rows valid (attended) after the append */
+  int32_t rebase_delta; /* D: retained K rotate by R(-D) before the append; 0 none */
+  int32_t compact_drop; /* rows dropped by this step's compaction; 0 none */
+  int32_t evict_slot;   /* REBASE: slot of the pushed-out token; -1 none */
+  int32_t window;
+  int32_t cap;
+  int32_t new_rows;
+  int32_t reserved[14];
+  double rope_new[RKV_MAX_NEW_ROWS][2][RKV_MAX_HEAD_DIM / 2]; /* cos, sin of (pos + j) theta_i */
+  double rope_delta[2][RKV_MAX_HEAD_DIM / 2];                 /* cos, sin of D theta_i */
+} rkv_step_plan;
+
+/* Where the cache lives (host struct describing device memory).
+ * Element (layer l, stream s, kv head g, slot r, e) of K is at
+ *   k + l*layer_stride + s*stream_stride + g*head_stride + r*slot_stride + e
+ * (strides in bfloat16 elements); V and k_lo use the same strides.
+ * The canonical layout is [L][S][Hkv][slots][d] with slot_stride = d. */
+typedef struct rkv_kv_view {
+  void* k;
+  void* v;
+  void* k_lo;             /* RKV_F_COMPENSATED only, else may be NULL */
+  int64_t layer_stride;
+  int64_t stream_stride;
+  int64_t head_stride;
+  int64_t slot_stride;    /* >= d */
+  int32_t slots;          /* rows allocated per (layer, stream, head) */
+  int32_t reserved;
+} rkv_kv_view;
+
+/* Library version (RKV_VERSION). */
+int rkv_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* rkv_strerror(int status);
+
+/* hipError_t of the last RKV_EHIP returned on the calling thread (0 if none). */
+int rkv_last_hip_error(void);
+
+/* Check a configuration without touching a device. */
+int rkv_validate_cfg(const rkv_cfg* cfg);
+
+/* Fill h_state[0..S) (host memory) for streams starting at h_origin[s] with
+ * window h_window[s] and capacity h_cap[s].  Required: REBASE cap == window;
+ * COMPACT cap > window (the voxtral.c window plus room to grow before the next
+ * compaction); ENC_CHUNK cap >= window + new_rows; origin >= 0.  The caller
+ * copies the array to device memory (S * sizeof(rkv_stream_state) bytes). */
+int rkv_state_init_host(const rkv_cfg* cfg, const int32_t* h_window,
+                        const int32_t* h_cap, const int64_t* h_origin,
+                        rkv_stream_state* h_state);
+
+/* Bytes of workspace rkv_decode_attn / rkv_decode_step /
+ * rkv_encoder_chunk_attn need for a cache of `slots` rows per head (0 when
+ * the key range is not split). */
+size_t rkv_workspace_bytes(const rkv_cfg* cfg, int32_t slots);
+
+/* Step plan (Audio8 explainer "Rolling KV Cache 三步拆解" steps 1-2; voxtral.c
+ * explainer section 二 trigger and logical position; section 三 encoder chunk):
+ * advance every stream by one step, update d_state in place and write
+ * d_plan[S] including the rotary cos/sin tables for the new row(s) and for
+ * the re-base angle.  Once per clock step, shared by all layers. */
+int rkv_advance(const rkv_cfg* cfg, rkv_stream_state* d_state,
+                rkv_step_plan* d_plan, void* hip_stream);
+
+/* Fused RoPE-on-append (voxtral.c explainer section 二: the rotation is baked
+ * into K when it is written).  For each (layer, stream, kv head) and new row
+ * j: K[slot_j] = rne(R(pos + j) k_new), V[slot_j] = v_new (and, compensated,
+ * k_lo[slot_j] = rne(R(pos + j) k_new - K[slot_j])), slot_j = (slot + j) mod cap.
+ * k_new, v_new: bfloat16 [L][S][Hkv][d] (ENC_CHUNK: [L][S][F][H][d]). */
+int rkv_append(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
+               const rkv_kv_view* kv, const void* k_new, const void* v_new,
+               void* hip_stream);
+
+/* Exact re-base (Audio8 explainer "Rolling KV Cache 三步拆解" step 2): for
+ * streams whose plan has rebase_delta D > 0, every retained K row (rows
+ * [0, n_valid) except the new row's slot) becomes rne(R(-D) K) in place
+ * (compensated: x = K + k_lo, K = rne(R(-D) x), k_lo = rne(R(-D) x - K)).
+ * REBASE mode only; call after rkv_advance and before rkv_append. */
+int rkv_roll_rebase(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
+                    const rkv_kv_view* kv, void* hip_stream);
+
+/* Compaction (voxtral.c explainer section 二): for streams whose plan has
+ * compact_drop D > 0, move K and V rows [D, D + window) to [0, window) in
+ * row order (an overlapping forward move, done in place).  COMPACT mode only;
+ * call after rkv_advance and before rkv_append. */
+int rkv_compact(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
+                const rkv_kv_view* kv, void* hip_stream);
+
+/* GQA decode attention over the cache (Audio8 explainer "Rolling KV Cache
+ * 三步拆解" step 3: attention scans only the fixed window).  For each layer,
+ * stream and query head h (KV head h / (Hq/Hkv)): out = softmax(scale *
+ * (R(pos) q_h) . K_r) V_r over rows r in [0, n_valid), with the query rotated
+ * at the plan's position.  q, out: [L][S][Hq][d].  Reads the cache as stored
+ * (call after rkv_append).  `workspace` may be NULL when
+ * rkv_workspace_bytes() is 0. */
+int rkv_decode_attn(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
+                    const rkv_kv_view* kv, const void* q, void* out,
+                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* One decoder step in a single pass over the cache: re-base (REBASE),
+ * append, and decode attention, with results identical to rkv_roll_rebase +
+ * rkv_append + rkv_decode_attn (COMPACT: rkv_compact must still run first). */
+int rkv_decode_step(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
+                    const rkv_kv_view* kv, const void* q, const void* k_new,
+                    const void* v_new, void* out, void* workspace,
+                    size_t workspace_bytes, void* hip_stream);
+
+/* Encoder chunk attention (voxtral.c explainer section 三: only the new
+ * positions are computed, against the cached K/V of the window).  Appends the
+ * F frames of the chunk (as rkv_append) and computes, for every head and frame
+ * j, attention over the frames at positions [first_pos, pos + j] held in the
+ * ring.  q, k_new, v_new, out: [L][S][F][H][d].  ENC_CHUNK mode only. */
+int rkv_encoder_chunk_attn(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
+                           const rkv_kv_view* kv, const void* q,
+                           const void* k_new, const void* v_new, void* out,
+                           void* workspace, size_t workspace_bytes,
+                           void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RKV_H */

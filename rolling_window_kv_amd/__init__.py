@@ -2,18 +2,15 @@
 
 The compute lives in ``librkv.so`` (hand-written HIP kernels behind a C ABI,
 declared in ``include/rkv.h``); :mod:`rolling_window_kv_amd.rkv` is the thin
-ctypes binding with the same entry-point names.  The binding is imported
-lazily so that :mod:`rolling_window_kv_amd.synth` can be used on its own.
+ctypes binding with the same entry-point names.  Submodules are imported on
+first use so that :mod:`rolling_window_kv_amd.synth` can be used on its own.
 """
+import importlib
 
-__all__ = ["rkv", "synth"]
+__all__ = ["rkv", "synth", "build"]
 
 
 def __getattr__(name):
-    if name == "rkv":
-        from . import rkv
-        return rkv
-    if name == "synth":
-        from . import synth
-        return synth
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

@@ -1,0 +1,267 @@
+// C entry points of librkv: argument validation on the host, then kernel
+// launches on the caller's stream.  Nothing here allocates device memory.
+
+#include <math.h>
+#include <string.h>
+
+#include "rkv_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return RKV_OK;
+  g_last_hip_error = (int)e;
+  return RKV_EHIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_cfg(const rkv_cfg* c) {
+  if (!c) return RKV_EINVAL;
+  if (c->num_streams < 1 || c->num_layers < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1)
+    return RKV_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return RKV_EUNSUPPORTED;
+  if (c->mode < RKV_MODE_REBASE || c->mode > RKV_MODE_ENC_CHUNK) return RKV_EUNSUPPORTED;
+  if (c->flags & ~(uint32_t)(RKV_F_COMPENSATED | RKV_F_OUT_F32)) return RKV_EUNSUPPORTED;
+  if (!(c->rope_base > 0.0) || !isfinite(c->rope_base)) return RKV_EINVAL;
+  if (!(c->softmax_scale >= 0.0f) || !isfinite(c->softmax_scale)) return RKV_EINVAL;
+  if (c->num_splits < 0) return RKV_EINVAL;
+  if (c->num_q_heads % c->num_kv_heads) return RKV_EINVAL;
+  const int64_t items = (int64_t)c->num_layers * c->num_streams * c->num_kv_heads;
+  if (items * 64 > (int64_t)1 << 31) return RKV_EUNSUPPORTED;
+  const int group = c->num_q_heads / c->num_kv_heads;
+  switch (c->mode) {
+    case RKV_MODE_REBASE:
+      if (c->rebase_chunk < 1) return RKV_EINVAL;
+      if (c->new_rows != 1) return RKV_EINVAL;
+      if (group > RKV_MAX_GROUP) return RKV_EUNSUPPORTED;
+      break;
+    case RKV_MODE_COMPACT:
+      if (c->new_rows != 1) return RKV_EINVAL;
+      if (group > RKV_MAX_GROUP) return RKV_EUNSUPPORTED;
+      if (c->flags & RKV_F_COMPENSATED) return RKV_EUNSUPPORTED;
+      break;
+    default:  // RKV_MODE_ENC_CHUNK
+      if (c->num_q_heads != c->num_kv_heads) return RKV_EINVAL;
+      if (c->new_rows < 1) return RKV_EINVAL;
+      if (c->new_rows > RKV_MAX_NEW_ROWS) return RKV_EUNSUPPORTED;
+      if (c->flags & RKV_F_COMPENSATED) return RKV_EUNSUPPORTED;
+      break;
+  }
+  return RKV_OK;
+}
+
+int check_kv(const rkv_cfg* c, const rkv_kv_view* kv) {
+  if (!kv || !kv->k || !kv->v) return RKV_EINVAL;
+  const bool comp = (c->flags & RKV_F_COMPENSATED) != 0;
+  if (comp && !kv->k_lo) return RKV_EINVAL;
+  if (kv->slots < 1) return RKV_EINVAL;
+  if (kv->slot_stride < c->head_dim || kv->layer_stride < 0 || kv->stream_stride < 0 ||
+      kv->head_stride < 0)
+    return RKV_EINVAL;
+  if (!aligned16(kv->k) || !aligned16(kv->v) || (comp && !aligned16(kv->k_lo)))
+    return RKV_EALIGN;
+  if ((kv->layer_stride | kv->stream_stride | kv->head_stride | kv->slot_stride) & 7)
+    return RKV_EALIGN;
+  return RKV_OK;
+}
+
+int check_ptr(const void* p) {
+  if (!p) return RKV_EINVAL;
+  if (!aligned16(p)) return RKV_EALIGN;
+  return RKV_OK;
+}
+
+rkv::RingArgs ring_of(const rkv_kv_view* kv) {
+  rkv::RingArgs r;
+  r.k = static_cast<uint16_t*>(kv->k);
+  r.v = static_cast<uint16_t*>(kv->v);
+  r.klo = static_cast<uint16_t*>(kv->k_lo);
+  r.ls = kv->layer_stride;
+  r.ss = kv->stream_stride;
+  r.hs = kv->head_stride;
+  r.rs = kv->slot_stride;
+  r.slots = kv->slots;
+  return r;
+}
+
+size_t workspace_for(const rkv_cfg* c, int32_t slots) {
+  const int n = rkv::choose_splits(c, slots);
+  if (n <= 1) return 0;
+  const int64_t items = (int64_t)c->num_layers * c->num_streams * c->num_kv_heads;
+  return (size_t)(items * n * rkv::partial_floats(c->head_dim) * (int64_t)sizeof(float));
+}
+
+int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
+              const rkv_kv_view* kv, const void* q, const void* knew, const void* vnew,
+              void* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (kind == rkv::kEncoderFused && cfg->mode != RKV_MODE_ENC_CHUNK) return RKV_EINVAL;
+  if (kind != rkv::kEncoderFused && cfg->mode == RKV_MODE_ENC_CHUNK) return RKV_EINVAL;
+  if ((rc = check_kv(cfg, kv))) return rc;
+  if (!plan) return RKV_EINVAL;
+  if ((rc = check_ptr(q)) || (rc = check_ptr(out))) return rc;
+  if (kind != rkv::kDecodeRead && ((rc = check_ptr(knew)) || (rc = check_ptr(vnew)))) return rc;
+  const size_t need = workspace_for(cfg, kv->slots);
+  if (need) {
+    if (!ws || ws_bytes < need) return RKV_ESPACE;
+    if (!aligned16(ws)) return RKV_EALIGN;
+  }
+  rkv::AttnArgs a;
+  a.plan = plan;
+  a.ring = ring_of(kv);
+  a.q = static_cast<const uint16_t*>(q);
+  a.knew = static_cast<const uint16_t*>(knew);
+  a.vnew = static_cast<const uint16_t*>(vnew);
+  a.out = out;
+  a.ws = static_cast<float*>(ws);
+  a.S = cfg->num_streams;
+  a.L = cfg->num_layers;
+  a.Hkv = cfg->num_kv_heads;
+  a.G = kind == rkv::kEncoderFused ? cfg->new_rows : cfg->num_q_heads / cfg->num_kv_heads;
+  a.F = cfg->new_rows;
+  a.nsplit = rkv::choose_splits(cfg, kv->slots);
+  a.out_f32 = (cfg->flags & RKV_F_OUT_F32) ? 1 : 0;
+  const double scale =
+      cfg->softmax_scale > 0.0f ? (double)cfg->softmax_scale : 1.0 / sqrt((double)cfg->head_dim);
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  return hip_status(rkv::launch_attention(cfg, kind, a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rkv_version(void) { return RKV_VERSION; }
+
+const char* rkv_strerror(int status) {
+  switch (status) {
+    case RKV_OK: return "ok";
+    case RKV_EINVAL: return "invalid argument";
+    case RKV_EUNSUPPORTED: return "unsupported configuration";
+    case RKV_EALIGN: return "pointer or stride not 16-byte aligned";
+    case RKV_ESTATE: return "stream state inconsistent with the mode";
+    case RKV_EHIP: return "HIP launch failed";
+    case RKV_ESPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int rkv_last_hip_error(void) { return g_last_hip_error; }
+
+int rkv_validate_cfg(const rkv_cfg* cfg) { return check_cfg(cfg); }
+
+int rkv_state_init_host(const rkv_cfg* cfg, const int32_t* h_window, const int32_t* h_cap,
+                        const int64_t* h_origin, rkv_stream_state* h_state) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!h_window || !h_cap || !h_origin || !h_state) return RKV_EINVAL;
+  for (int s = 0; s < cfg->num_streams; ++s) {
+    const int32_t W = h_window[s], cap = h_cap[s];
+    const int64_t origin = h_origin[s];
+    if (W < 1 || cap < 1 || origin < 0) return RKV_ESTATE;
+    switch (cfg->mode) {
+      case RKV_MODE_REBASE:
+        if (cap != W) return RKV_ESTATE;
+        break;
+      case RKV_MODE_COMPACT:
+        if (cap <= W) return RKV_ESTATE;
+        break;
+      default:
+        if (cap < W + cfg->new_rows) return RKV_ESTATE;
+        break;
+    }
+  }
+  for (int s = 0; s < cfg->num_streams; ++s) {
+    rkv_stream_state& st = h_state[s];
+    memset(&st, 0, sizeof(st));
+    st.t = h_origin[s] - 1;
+    st.origin = h_origin[s];
+    st.pos_offset = cfg->mode == RKV_MODE_REBASE
+                        ? (int64_t)cfg->rebase_chunk * (h_origin[s] / cfg->rebase_chunk)
+                        : h_origin[s];
+    st.len = 0;
+    st.window = h_window[s];
+    st.cap = h_cap[s];
+  }
+  return RKV_OK;
+}
+
+size_t rkv_workspace_bytes(const rkv_cfg* cfg, int32_t slots) {
+  if (check_cfg(cfg) || slots < 1) return 0;
+  return workspace_for(cfg, slots);
+}
+
+int rkv_advance(const rkv_cfg* cfg, rkv_stream_state* d_state, rkv_step_plan* d_plan,
+                void* hip_stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!d_state || !d_plan) return RKV_EINVAL;
+  if (((uintptr_t)d_state & 7u) || !aligned16(d_plan)) return RKV_EALIGN;
+  return hip_status(rkv::launch_advance(cfg, d_state, d_plan, static_cast<hipStream_t>(hip_stream)));
+}
+
+int rkv_append(const rkv_cfg* cfg, const rkv_step_plan* d_plan, const rkv_kv_view* kv,
+               const void* k_new, const void* v_new, void* hip_stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if ((rc = check_kv(cfg, kv))) return rc;
+  if (!d_plan) return RKV_EINVAL;
+  if ((rc = check_ptr(k_new)) || (rc = check_ptr(v_new))) return rc;
+  return hip_status(rkv::launch_append(cfg, d_plan, ring_of(kv), static_cast<const uint16_t*>(k_new),
+                                       static_cast<const uint16_t*>(v_new),
+                                       static_cast<hipStream_t>(hip_stream)));
+}
+
+int rkv_roll_rebase(const rkv_cfg* cfg, const rkv_step_plan* d_plan, const rkv_kv_view* kv,
+                    void* hip_stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (cfg->mode != RKV_MODE_REBASE) return RKV_EINVAL;
+  if ((rc = check_kv(cfg, kv))) return rc;
+  if (!d_plan) return RKV_EINVAL;
+  return hip_status(rkv::launch_rebase(cfg, d_plan, ring_of(kv), static_cast<hipStream_t>(hip_stream)));
+}
+
+int rkv_compact(const rkv_cfg* cfg, const rkv_step_plan* d_plan, const rkv_kv_view* kv,
+                void* hip_stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (cfg->mode != RKV_MODE_COMPACT) return RKV_EINVAL;
+  if ((rc = check_kv(cfg, kv))) return rc;
+  if (!d_plan) return RKV_EINVAL;
+  return hip_status(rkv::launch_compact(cfg, d_plan, ring_of(kv), static_cast<hipStream_t>(hip_stream)));
+}
+
+int rkv_decode_attn(const rkv_cfg* cfg, const rkv_step_plan* d_plan, const rkv_kv_view* kv,
+                    const void* q, void* out, void* workspace, size_t workspace_bytes,
+                    void* hip_stream) {
+  return attention(cfg, rkv::kDecodeRead, d_plan, kv, q, nullptr, nullptr, out, workspace,
+                   workspace_bytes, hip_stream);
+}
+
+int rkv_decode_step(const rkv_cfg* cfg, const rkv_step_plan* d_plan, const rkv_kv_view* kv,
+                    const void* q, const void* k_new, const void* v_new, void* out,
+                    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return attention(cfg, rkv::kDecodeFused, d_plan, kv, q, k_new, v_new, out, workspace,
+                   workspace_bytes, hip_stream);
+}
+
+int rkv_encoder_chunk_attn(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
+                           const rkv_kv_view* kv, const void* q, const void* k_new,
+                           const void* v_new, void* out, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+  return attention(cfg, rkv::kEncoderFused, d_plan, kv, q, k_new, v_new, out, workspace,
+                   workspace_bytes, hip_stream);
+}
+
+}  // extern "C"
+
+static_assert(sizeof(rkv_cfg) == 56, "rkv_cfg layout");
+static_assert(sizeof(rkv_stream_state) == 48, "rkv_stream_state layout");
+static_assert(offsetof(rkv_step_plan, rope_new) == 128, "rkv_step_plan header");
+static_assert(sizeof(rkv_step_plan) == 128 + 8192 + 1024, "rkv_step_plan layout");
+static_assert(sizeof(rkv_kv_view) == 64, "rkv_kv_view layout");

@@ -1,0 +1,532 @@
+// Windowed attention over the rolling cache on gfx950 matrix cores.
+//
+// One workgroup handles one (layer, stream, kv head) item -- or one split of
+// its key range -- with NW waves that take 16-key tiles in turn, each wave
+// loading its next tile while it computes the current one.  The G query
+// vectors that share the KV head (the 8 query heads of a GQA group, or the F
+// frames of an encoder chunk) form the N side of the matrix-core products:
+//
+//   scores  S[key][col] = K[key][:] . Qt[:][col]   v_mfma_f32_16x16x32_bf16
+//   output  O[d][col]  += Vt[d][key] . P[key][col]  v_mfma_f32_16x16x16_bf16
+//
+// Only 8 of the 16 columns are query vectors, so the other 8 carry the
+// bfloat16 rounding residual of the same vectors: column c < 8 holds
+// hi = rne(x) and column c + 8 holds lo = rne(x - hi), for the rotated query
+// and for the probabilities.  Adding the two columns (a row_ror:8 DPP move)
+// gives scores and outputs at about 16-bit operand precision at no extra
+// matrix-core work.  K and V are the stored bfloat16 values.
+//
+// Lane layout (lane = 16*g4 + c).  Score MFMA: A holds K row key0+c, dims
+// 32*st + 8*g4 .. +7; B holds query column c, the same dims; the result holds
+// keys key0 + 4*g4 + r (r < 4) of column c -- exactly the B layout of the
+// 16x16x16 probability MFMA (k = 4*g4 .. 4*g4+3).  V rows key0 + 4*g4 + j
+// (j < 4) are loaded row-contiguously (lane reads dims CW*c .. CW*c+CW-1, so
+// each load instruction covers four whole rows) and transposed in registers
+// into the A operand (row c <-> dim CW*c + e for product e).  Output lane
+// (g4, c < 8) ends with dims [4*CW*g4, 4*CW*g4 + 4*CW) of query column c.
+//
+// Softmax is online with a lazily moved maximum: probabilities use the
+// running maximum m until a tile's maximum exceeds it by more than 2^8 (in
+// log2 units), so rescaling of the accumulators is rare; the result is the
+// same softmax.
+//
+// The fused kinds also update the cache in the same launch, with results
+// identical to running rkv_roll_rebase, rkv_append and the read-only kind in
+// turn: before its attention loop each wave rotates the new row(s) of its
+// tiles from k_new in float64 and writes them (RoPE-on-append), and in REBASE
+// mode, when the plan's delta D > 0, rotates every other retained row of its
+// tiles by R(-D) in float64 and writes it back (exact re-base).
+
+#include "rkv_device.h"
+#include "rkv_internal.h"
+
+namespace rkv {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float dpp_ror8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CW>
+struct VChunk;
+template <>
+struct VChunk<8> {
+  typedef u32x4 T;
+  static __device__ __forceinline__ T load(const uint16_t* p) { return ld16(p); }
+  static __device__ __forceinline__ void store(uint16_t* p, const T& w) { st16(p, w); }
+  static __device__ __forceinline__ T zero() { return u32x4{0u, 0u, 0u, 0u}; }
+  static __device__ __forceinline__ uint32_t elem(const T& w, int e) {
+    return (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+  }
+};
+template <>
+struct VChunk<4> {
+  typedef u32x2 T;
+  static __device__ __forceinline__ T load(const uint16_t* p) { return ld8(p); }
+  static __device__ __forceinline__ void store(uint16_t* p, const T& w) { st8(p, w); }
+  static __device__ __forceinline__ T zero() { return u32x2{0u, 0u}; }
+  static __device__ __forceinline__ uint32_t elem(const T& w, int e) {
+    return (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+  }
+};
+
+constexpr float kLazyMax = 8.0f;  // rescale only when the max grows by > 2^8
+
+// Waves per SIMD the register allocation targets: the largest count that
+// fits without spilling (the compensated re-base keeps two more K arrays live).
+template <int D, bool COMP>
+struct Occupancy {
+  static constexpr int waves = D == 128 ? (COMP ? 2 : 3) : (COMP ? 3 : 4);
+};
+
+template <int D, int NW, int KIND, bool COMP>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(Occupancy<D, COMP>::waves)))
+void attn_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;    // k-steps of the score MFMA (32 dims each)
+  constexpr int KH = KS / 2;    // k-steps of the first half (pair partner is st + KH)
+  constexpr int CW = D / 16;    // V elements per lane per row = probability MFMAs per tile
+  constexpr int TK = 16;        // keys per tile
+  typedef VChunk<CW> VC;
+  typedef typename VC::T VT;
+
+  __shared__ float sm_m[NW][8];
+  __shared__ float sm_l[NW][8];
+  __shared__ float sm_o[NW][8][D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15;
+  const int g4 = lane >> 4;
+  const int col_q = c & 7;       // query vector of this column
+  const int part = c >> 3;       // 0: hi, 1: lo residual
+
+  const int split = blockIdx.x % a.nsplit;
+  const int item = blockIdx.x / a.nsplit;
+  const int g = item % a.Hkv;
+  const int s = (item / a.Hkv) % a.S;
+  const int l = item / (a.Hkv * a.S);
+  const rkv_step_plan* P = a.plan + s;
+
+  const int slots = a.ring.slots;
+  const int per = (((slots + a.nsplit - 1) / a.nsplit) + TK - 1) & ~(TK - 1);
+  const int kb = split * per;
+  const int kalloc = kb + per < slots ? kb + per : slots;
+
+  const int64_t rbase = (int64_t)l * a.ring.ls + (int64_t)s * a.ring.ss + (int64_t)g * a.ring.hs;
+  uint16_t* __restrict__ Kp = a.ring.k + rbase;
+  uint16_t* __restrict__ Vp = a.ring.v + rbase;
+  uint16_t* __restrict__ Lp = COMP ? a.ring.klo + rbase : nullptr;
+  const int64_t rs = a.ring.rs;
+
+  // Offsets of query vector j in the [L][S][Hkv*G][D] (decoder) or
+  // [L][S][F][H][D] (encoder) inputs and outputs, and of new K/V row j in
+  // [L][S][Hkv][D] (decoder) or [L][S][F][H][D] (encoder).
+  auto vec_off = [&](int j) -> int64_t {
+    if (KIND == kEncoderFused) return ((((int64_t)l * a.S + s) * a.F + j) * a.Hkv + g) * D;
+    return ((((int64_t)l * a.S + s) * a.Hkv + g) * a.G + j) * D;
+  };
+  auto new_off = [&](int j) -> int64_t {
+    if (KIND == kEncoderFused) return vec_off(j);
+    return (((int64_t)l * a.S + s) * a.Hkv + g) * D;
+  };
+
+  // ---- tile loads (rows clamped into the allocation; masked later) ----
+  struct Tile {
+    u32x4 k[KS];
+    VT v[4];
+  };
+  auto load_tile = [&](int key0, Tile& T) {
+    const int rk = key0 + c < slots ? key0 + c : slots - 1;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) T.k[st] = ld16(Kp + rk * rs + 32 * st + 8 * g4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rv0 = key0 + 4 * g4 + j;
+      const int rv = rv0 < slots ? rv0 : slots - 1;
+      T.v[j] = VC::load(Vp + rv * rs + CW * c);
+    }
+  };
+
+  // The first tile is requested before the plan is read.
+  Tile t0, t1;
+  int tile = wave;
+  if (kb + TK * tile < kalloc) load_tile(kb + TK * tile, t0);
+
+  const int n_valid = P->n_valid < slots ? P->n_valid : slots;
+  const int ke = kb + per < n_valid ? kb + per : n_valid;
+
+  // ---- rotated query, split into hi/lo bfloat16 columns (B operand) ----
+  bf16x8 qop[KS];
+  {
+    const bool has = col_q < a.G;
+    const uint16_t* qp = a.q + vec_off(has ? col_q : 0);
+    const int rrow = (KIND == kEncoderFused) ? col_q : 0;
+    u32x4 qraw[KS];
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      qraw[st] = has ? ld16(qp + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int st = 0; st < KH; ++st) {
+      u32x4 w1, w2;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t o1 = 0, o2 = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = 2 * w + h;
+          const int i = 32 * st + 8 * g4 + e;
+          double y1, y2;
+          rotate_pair64(bf2f(elem8(qraw[st], e)), bf2f(elem8(qraw[st + KH], e)),
+                        P->rope_new[rrow][0][i], P->rope_new[rrow][1][i], y1, y2);
+          const uint32_t h1 = f64_to_bf16(y1), h2 = f64_to_bf16(y2);
+          const uint32_t b1 = part ? f64_to_bf16(y1 - (double)bf2f(h1)) : h1;
+          const uint32_t b2 = part ? f64_to_bf16(y2 - (double)bf2f(h2)) : h2;
+          o1 |= b1 << (16 * h);
+          o2 |= b2 << (16 * h);
+        }
+        w1[w] = o1;
+        w2[w] = o2;
+      }
+      qop[st] = __builtin_bit_cast(bf16x8, w1);
+      qop[st + KH] = __builtin_bit_cast(bf16x8, w2);
+    }
+  }
+
+  // ---- fused-update parameters ----
+  const int delta = (KIND == kDecodeFused) ? P->rebase_delta : 0;
+  const int slot_new = P->slot;
+  const int nnew = P->new_rows;
+  const int cap = P->cap;
+  const int64_t last_pos = P->t;                      // encoder mask bookkeeping
+  const int slot_last = (slot_new + nnew - 1) % cap;
+  const int64_t first_pos = P->first_pos;
+  const int64_t qpos = P->pos + col_q;
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4 oacc[CW];
+#pragma unroll
+  for (int e = 0; e < CW; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto new_index = [&](int row) -> int {
+    if (KIND == kDecodeFused) return row == slot_new ? 0 : -1;
+    const int dj = (row - slot_new + cap) % cap;
+    return dj < nnew ? dj : -1;
+  };
+
+  // Rotate this lane's K chunks of one row in float64 and store them; pairs
+  // are chunks (st, st + KH).  src: chunks to rotate (k_new or the stored
+  // row); lo: stored residual (compensated re-base); sgn = -1 rotates by -angle.
+  auto rotate_row = [&](u32x4* kk, const u32x4* src, const u32x4* lo, const double* cs,
+                        const double* sn, double sgn, int row) {
+#pragma unroll
+    for (int st = 0; st < KH; ++st) {
+      u32x4 w1, w2, r1, r2;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t o1 = 0, o2 = 0, p1 = 0, p2 = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = 2 * w + h;
+          const int i = 32 * st + 8 * g4 + e;
+          double x1 = bf2f(elem8(src[st], e)), x2 = bf2f(elem8(src[st + KH], e));
+          if (COMP && lo) {
+            x1 += (double)bf2f(elem8(lo[st], e));
+            x2 += (double)bf2f(elem8(lo[st + KH], e));
+          }
+          double y1, y2;
+          rotate_pair64(x1, x2, cs[i], sgn * sn[i], y1, y2);
+          const uint32_t h1 = f64_to_bf16(y1), h2 = f64_to_bf16(y2);
+          o1 |= h1 << (16 * h);
+          o2 |= h2 << (16 * h);
+          if (COMP) {
+            p1 |= f64_to_bf16(y1 - (double)bf2f(h1)) << (16 * h);
+            p2 |= f64_to_bf16(y2 - (double)bf2f(h2)) << (16 * h);
+          }
+        }
+        w1[w] = o1;
+        w2[w] = o2;
+        r1[w] = p1;
+        r2[w] = p2;
+      }
+      kk[st] = w1;
+      kk[st + KH] = w2;
+      st16(Kp + row * rs + 32 * st + 8 * g4, w1);
+      st16(Kp + row * rs + 32 * (st + KH) + 8 * g4, w2);
+      if (COMP) {
+        st16(Lp + row * rs + 32 * st + 8 * g4, r1);
+        st16(Lp + row * rs + 32 * (st + KH) + 8 * g4, r2);
+      }
+    }
+  };
+
+  auto process = [&](Tile& T, int key0) {
+    // ---- scores ----
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[st]), qop[st],
+                                                    acc, 0, 0, 0);
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = (acc[r] + dpp_ror8(acc[r])) * a.scale_log2;
+      const int row = key0 + 4 * g4 + r;
+      bool vis = row < ke;
+      if (KIND == kEncoderFused) {
+        const int back = (slot_last - row + cap) % cap;
+        const int64_t kpos = last_pos - back;
+        vis = vis && kpos >= first_pos && kpos <= qpos;
+      }
+      x = vis ? x : -INFINITY;
+      sv[r] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = mx > m_run + kLazyMax;
+    if (__any(need)) {
+      const float alpha = need ? fast_exp2(m_run - mx) : 1.f;  // exp2(-inf) = 0
+      if (need) m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < CW; ++e) oacc[e] *= alpha;
+    }
+    float pj[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pj[r] = m_run == -INFINITY ? 0.f : fast_exp2(sv[r] - m_run);
+    l_run += (pj[0] + pj[1]) + (pj[2] + pj[3]);
+    uint32_t pw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t b[2];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const float p = pj[2 * h + q2];
+        const uint32_t hi = f2bf(p);
+        b[q2] = part ? f2bf(p - bf2f(hi)) : hi;
+      }
+      pw[h] = b[0] | (b[1] << 16);
+    }
+    const s16x4 pop = __builtin_bit_cast(s16x4, u32x2{pw[0], pw[1]});
+
+    // ---- V^T operand (register transpose) and output accumulation ----
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (key0 + 4 * g4 + j >= ke) T.v[j] = VC::zero();
+#pragma unroll
+    for (int e = 0; e < CW; ++e) {
+      const uint32_t w0 = VC::elem(T.v[0], e) | (VC::elem(T.v[1], e) << 16);
+      const uint32_t w1 = VC::elem(T.v[2], e) | (VC::elem(T.v[3], e) << 16);
+      oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{w0, w1}),
+                                                           pop, oacc[e], 0, 0, 0);
+    }
+  };
+
+  // ---- fused cache updates: a pre-pass over this wave's own tiles ----
+  // Re-base (every retained row of the wave's tiles) and append (the new
+  // rows) are written before the attention loop; the loop then reads the
+  // updated rows back.  Tiles are owned by one wave, so no barrier is needed.
+  if (KIND != kDecodeRead) {
+    bool touched_first = false;
+    for (int tt = wave;; tt += NW) {
+      const int key0 = kb + TK * tt;
+      if (key0 >= ke) break;
+      bool any_new = false;
+      if (KIND == kDecodeFused) any_new = slot_new >= key0 && slot_new < key0 + TK;
+      else any_new = true;
+      if (delta == 0 && !any_new) continue;
+      if (tt == wave) touched_first = true;
+      const int row = key0 + c;
+      if (row < ke) {
+        const int jn = new_index(row);
+        if (jn >= 0) {
+          u32x4 src[KS], kk[KS];
+          const uint16_t* kn = a.knew + new_off(jn);
+#pragma unroll
+          for (int st = 0; st < KS; ++st) src[st] = ld16(kn + 32 * st + 8 * g4);
+          rotate_row(kk, src, nullptr, P->rope_new[jn][0], P->rope_new[jn][1], 1.0, row);
+        } else if (delta != 0) {
+          u32x4 src[KS], lo[KS], kk[KS];
+#pragma unroll
+          for (int st = 0; st < KS; ++st) {
+            src[st] = ld16(Kp + row * rs + 32 * st + 8 * g4);
+            lo[st] = COMP ? ld16(Lp + row * rs + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
+          }
+          rotate_row(kk, src, COMP ? lo : nullptr, P->rope_delta[0], P->rope_delta[1], -1.0,
+                     row);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rv = key0 + 4 * g4 + j;
+        if (rv >= ke) continue;
+        const int jn = new_index(rv);
+        if (jn >= 0) VC::store(Vp + rv * rs + CW * c, VC::load(a.vnew + new_off(jn) + CW * c));
+      }
+    }
+    // the early request of the first tile predates these stores
+    if (touched_first) load_tile(kb + TK * wave, t0);
+  }
+
+  // ---- main loop: two tiles in registers, the next one loading ----
+  for (;;) {
+    const int key0 = kb + TK * tile;
+    if (key0 >= ke) break;
+    int nxt = tile + NW;
+    if (kb + TK * nxt < ke) load_tile(kb + TK * nxt, t1);
+    process(t0, key0);
+    tile = nxt;
+    const int key1 = kb + TK * tile;
+    if (key1 >= ke) break;
+    nxt = tile + NW;
+    if (kb + TK * nxt < ke) load_tile(kb + TK * nxt, t0);
+    process(t1, key1);
+    tile = nxt;
+  }
+
+  // ---- per-wave reduction: row sums over lane groups, hi+lo columns ----
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+  for (int e = 0; e < CW; ++e)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) oacc[e][r] += dpp_ror8(oacc[e][r]);
+
+  if (c < 8) {
+    if (g4 == 0) {
+      sm_m[wave][c] = m_run;
+      sm_l[wave][c] = l_run;
+    }
+#pragma unroll
+    for (int e = 0; e < CW; ++e)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm_o[wave][c][CW * (4 * g4 + r) + e] = oacc[e][r];
+  }
+  __syncthreads();
+
+  // ---- merge waves; write output or split partial ----
+  const int total = a.G * D;
+  for (int idx = threadIdx.x; idx < total; idx += NW * 64) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_m[w][h];
+        const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+        num += f * sm_o[w][h][d];
+        den += f * sm_l[w][h];
+      }
+    }
+    if (a.nsplit == 1) {
+      const float o = den > 0.f ? num / den : 0.f;
+      const int64_t off = vec_off(h) + d;
+      if (a.out_f32) reinterpret_cast<float*>(a.out)[off] = o;
+      else reinterpret_cast<uint16_t*>(a.out)[off] = (uint16_t)f2bf(o);
+    } else {
+      float* pp = a.ws + ((int64_t)item * a.nsplit + split) * partial_floats(D);
+      if (d == 0) {
+        pp[h] = M;
+        pp[8 + h] = den;
+      }
+      pp[16 + h * D + d] = num;
+    }
+  }
+}
+
+// Merge the split partials of one item: out = sum_j 2^(m_j - M) num_j / sum_j 2^(m_j - M) l_j.
+template <int D, int KIND>
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+  const int item = blockIdx.x;
+  const int g = item % a.Hkv;
+  const int s = (item / a.Hkv) % a.S;
+  const int l = item / (a.Hkv * a.S);
+  const float* base = a.ws + (int64_t)item * a.nsplit * partial_floats(D);
+  const int total = a.G * D;
+  for (int idx = threadIdx.x; idx < total; idx += 256) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float M = -INFINITY;
+    for (int j = 0; j < a.nsplit; ++j) M = fmaxf(M, base[j * partial_floats(D) + h]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+      for (int j = 0; j < a.nsplit; ++j) {
+        const float* pp = base + j * partial_floats(D);
+        const float mj = pp[h];
+        const float f = mj == -INFINITY ? 0.f : fast_exp2(mj - M);
+        num += f * pp[16 + h * D + d];
+        den += f * pp[8 + h];
+      }
+    }
+    const float o = den > 0.f ? num / den : 0.f;
+    int64_t off;
+    if (KIND == kEncoderFused) off = ((((int64_t)l * a.S + s) * a.F + h) * a.Hkv + g) * D + d;
+    else off = ((((int64_t)l * a.S + s) * a.Hkv + g) * a.G + h) * D + d;
+    if (a.out_f32) reinterpret_cast<float*>(a.out)[off] = o;
+    else reinterpret_cast<uint16_t*>(a.out)[off] = (uint16_t)f2bf(o);
+  }
+}
+
+constexpr int kWavesPerGroup = 4;
+
+template <int D, int KIND, bool COMP>
+hipError_t launch_kind(const AttnArgs& args, int items, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_kernel<D, kWavesPerGroup, KIND, COMP>), dim3(items * args.nsplit),
+                     dim3(kWavesPerGroup * 64), 0, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || args.nsplit == 1) return e;
+  hipLaunchKernelGGL((combine_kernel<D, KIND>), dim3(items), dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(AttnKind kind, bool comp, const AttnArgs& args, int items,
+                    hipStream_t stream) {
+  switch (kind) {
+    case kDecodeRead:
+      return launch_kind<D, kDecodeRead, false>(args, items, stream);
+    case kDecodeFused:
+      return comp ? launch_kind<D, kDecodeFused, true>(args, items, stream)
+                  : launch_kind<D, kDecodeFused, false>(args, items, stream);
+    default:
+      return launch_kind<D, kEncoderFused, false>(args, items, stream);
+  }
+}
+
+}  // namespace
+
+int choose_splits(const rkv_cfg* cfg, int32_t slots) {
+  if (cfg->num_splits > 0) {
+    const int max_split = (slots + 15) / 16;
+    return cfg->num_splits < max_split ? cfg->num_splits : (max_split > 0 ? max_split : 1);
+  }
+  const int64_t items = (int64_t)cfg->num_layers * cfg->num_streams * cfg->num_kv_heads;
+  const int64_t target = 2048;
+  int64_t n = (target + items - 1) / items;
+  const int64_t max_split = (slots + 63) / 64;
+  if (n > max_split) n = max_split;
+  if (n > 64) n = 64;
+  if (n < 1) n = 1;
+  return (int)n;
+}
+
+hipError_t launch_attention(const rkv_cfg* cfg, AttnKind kind, const AttnArgs& args,
+                            hipStream_t stream) {
+  const int items = cfg->num_layers * cfg->num_streams * cfg->num_kv_heads;
+  const bool comp = (cfg->flags & RKV_F_COMPENSATED) != 0;
+  if (cfg->head_dim == 128) return launch_d<128>(kind, comp, args, items, stream);
+  return launch_d<64>(kind, comp, args, items, stream);
+}
+
+}  // namespace rkv

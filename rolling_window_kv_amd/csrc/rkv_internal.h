@@ -1,0 +1,53 @@
+// Host-side launch interfaces between the C entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rkv.h"
+
+namespace rkv {
+
+struct RingArgs {
+  uint16_t* k;
+  uint16_t* v;
+  uint16_t* klo;
+  int64_t ls, ss, hs, rs;  // layer / stream / head / slot strides (elements)
+  int32_t slots;
+};
+
+struct AttnArgs {
+  const rkv_step_plan* plan;
+  RingArgs ring;
+  const uint16_t* q;
+  const uint16_t* knew;
+  const uint16_t* vnew;
+  void* out;
+  float* ws;          // split partials (nsplit > 1)
+  int32_t S, L, Hkv;  // streams, layers, KV heads (ENC: heads)
+  int32_t G;          // query vectors per KV head (decoder: Hq/Hkv; ENC: F)
+  int32_t F;          // frames per chunk (ENC), 1 otherwise
+  int32_t nsplit;
+  int32_t out_f32;
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+enum AttnKind { kDecodeRead = 0, kDecodeFused = 1, kEncoderFused = 2 };
+
+// Number of key-range splits for an attention call.
+int choose_splits(const rkv_cfg* cfg, int32_t slots);
+// Floats of workspace per (item, split) partial.
+__host__ __device__ inline int64_t partial_floats(int d) { return 16 + 8 * (int64_t)d; }
+
+hipError_t launch_advance(const rkv_cfg* cfg, rkv_stream_state* st, rkv_step_plan* plan,
+                          hipStream_t stream);
+hipError_t launch_append(const rkv_cfg* cfg, const rkv_step_plan* plan, const RingArgs& ring,
+                         const uint16_t* knew, const uint16_t* vnew, hipStream_t stream);
+hipError_t launch_rebase(const rkv_cfg* cfg, const rkv_step_plan* plan, const RingArgs& ring,
+                         hipStream_t stream);
+hipError_t launch_compact(const rkv_cfg* cfg, const rkv_step_plan* plan, const RingArgs& ring,
+                          hipStream_t stream);
+hipError_t launch_attention(const rkv_cfg* cfg, AttnKind kind, const AttnArgs& args,
+                            hipStream_t stream);
+
+}  // namespace rkv

@@ -1,0 +1,215 @@
+// Cache updates: RoPE-on-append, in-place exact re-base, compaction move.
+
+#include "rkv_device.h"
+#include "rkv_internal.h"
+
+namespace rkv {
+namespace {
+
+__device__ __forceinline__ void item_coords(int item, int H, int S, int& l, int& s, int& g) {
+  g = item % H;
+  s = (item / H) % S;
+  l = item / (H * S);
+}
+
+// ---------------------------------------------------------------------------
+// Append (voxtral.c explainer, section 二: K is stored with its rotation baked
+// in).  One wave per (layer, stream, kv head, new row); lane i owns rotary
+// pair i (elements i and i + d/2) and V elements 2i, 2i+1.
+// ---------------------------------------------------------------------------
+template <int D, bool COMP, bool ENC>
+__global__ __launch_bounds__(64) void append_kernel(const rkv_step_plan* __restrict__ plan,
+                                                    RingArgs ring,
+                                                    const uint16_t* __restrict__ knew,
+                                                    const uint16_t* __restrict__ vnew, int S,
+                                                    int H, int F) {
+  constexpr int HALF = D / 2;
+  int l, s, g;
+  item_coords(blockIdx.x, H, S, l, s, g);
+  const int j = blockIdx.y;
+  const rkv_step_plan* P = plan + s;
+  if (j >= P->new_rows) return;
+  const int slot = (P->slot + j) % P->cap;
+  if (slot >= ring.slots) return;  // state capacity beyond the allocated rows
+  const int64_t in_off =
+      ENC ? ((((int64_t)l * S + s) * F + j) * H + g) * D : (((int64_t)l * S + s) * H + g) * D;
+  const int64_t row = (int64_t)l * ring.ls + (int64_t)s * ring.ss + (int64_t)g * ring.hs +
+                      (int64_t)slot * ring.rs;
+  const int i = threadIdx.x;
+  if (i < HALF) {
+    const double x1 = bf2f(knew[in_off + i]);
+    const double x2 = bf2f(knew[in_off + i + HALF]);
+    double y1, y2;
+    rotate_pair64(x1, x2, P->rope_new[j][0][i], P->rope_new[j][1][i], y1, y2);
+    const uint32_t h1 = f64_to_bf16(y1), h2 = f64_to_bf16(y2);
+    ring.k[row + i] = (uint16_t)h1;
+    ring.k[row + i + HALF] = (uint16_t)h2;
+    if (COMP) {
+      ring.klo[row + i] = (uint16_t)f64_to_bf16(y1 - (double)bf2f(h1));
+      ring.klo[row + i + HALF] = (uint16_t)f64_to_bf16(y2 - (double)bf2f(h2));
+    }
+    const uint32_t vv = *reinterpret_cast<const uint32_t*>(vnew + in_off + 2 * i);
+    *reinterpret_cast<uint32_t*>(ring.v + row + 2 * i) = vv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact re-base (Audio8 explainer, "Rolling KV Cache 三步拆解" step 2): every
+// retained K row is rotated by R(-D) in place.  A thread owns 8 rotary pairs
+// of one row: 16 bytes from each half of the row.
+// ---------------------------------------------------------------------------
+template <int D, bool COMP>
+__global__ __launch_bounds__(256) void rebase_kernel(const rkv_step_plan* __restrict__ plan,
+                                                     RingArgs ring, int S, int H) {
+  constexpr int HALF = D / 2;
+  constexpr int TPR = HALF / 8;       // threads per row
+  constexpr int RPB = 256 / TPR;      // rows per block
+  int l, s, g;
+  item_coords(blockIdx.x, H, S, l, s, g);
+  const rkv_step_plan* P = plan + s;
+  if (P->rebase_delta == 0) return;
+  const int r = blockIdx.y * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  const int n_valid = P->n_valid < ring.slots ? P->n_valid : ring.slots;
+  if (r >= n_valid || r == P->slot) return;
+  const int64_t row = (int64_t)l * ring.ls + (int64_t)s * ring.ss + (int64_t)g * ring.hs +
+                      (int64_t)r * ring.rs;
+  uint16_t* k1 = ring.k + row + 8 * c;
+  uint16_t* k2 = k1 + HALF;
+  const u32x4 a = ld16(k1), b = ld16(k2);
+  u32x4 la = {0u, 0u, 0u, 0u}, lb = {0u, 0u, 0u, 0u};
+  if (COMP) {
+    la = ld16(ring.klo + row + 8 * c);
+    lb = ld16(ring.klo + row + 8 * c + HALF);
+  }
+  u32x4 ha, hb, ra, rb;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t wa = 0, wb = 0, wla = 0, wlb = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * w + h;
+      const int i = 8 * c + e;
+      double x1 = bf2f(elem8(a, e)), x2 = bf2f(elem8(b, e));
+      if (COMP) {
+        x1 += (double)bf2f(elem8(la, e));
+        x2 += (double)bf2f(elem8(lb, e));
+      }
+      double y1, y2;
+      rotate_pair64(x1, x2, P->rope_delta[0][i], -P->rope_delta[1][i], y1, y2);
+      const uint32_t h1 = f64_to_bf16(y1), h2 = f64_to_bf16(y2);
+      wa |= h1 << (16 * h);
+      wb |= h2 << (16 * h);
+      if (COMP) {
+        wla |= f64_to_bf16(y1 - (double)bf2f(h1)) << (16 * h);
+        wlb |= f64_to_bf16(y2 - (double)bf2f(h2)) << (16 * h);
+      }
+    }
+    ha[w] = wa;
+    hb[w] = wb;
+    ra[w] = wla;
+    rb[w] = wlb;
+  }
+  st16(k1, ha);
+  st16(k2, hb);
+  if (COMP) {
+    st16(ring.klo + row + 8 * c, ra);
+    st16(ring.klo + row + 8 * c + HALF, rb);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Compaction move (voxtral.c explainer, section 二): rows [drop, drop + W) go
+// to [0, W) in row order.  The ranges overlap, so one wave moves a column
+// group of every row front to back in batches of at most `drop` rows: each
+// batch reads rows that no earlier batch wrote and writes rows whose reads
+// have completed, which makes the in-place forward move safe.  Column groups
+// (and K versus V) are independent, giving the parallelism.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void compact_kernel(const rkv_step_plan* __restrict__ plan,
+                                                     RingArgs ring, int S, int H) {
+  constexpr int CG = 4;                 // column groups per row
+  constexpr int LPR = D / (8 * CG);     // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;         // rows per load instruction
+  constexpr int NB = 4;                 // loads in flight per lane
+  int l, s, g;
+  item_coords(blockIdx.x, H, S, l, s, g);
+  const rkv_step_plan* P = plan + s;
+  const int drop = P->compact_drop;
+  if (drop == 0 || P->cap > ring.slots) return;
+  const int rows = P->window;
+  uint16_t* base = (blockIdx.z == 0 ? ring.k : ring.v) + (int64_t)l * ring.ls +
+                   (int64_t)s * ring.ss + (int64_t)g * ring.hs;
+  const int lane = threadIdx.x;
+  const int col = blockIdx.y * (D / CG) + (lane % LPR) * 8;
+  const int ro = lane / LPR;
+  const int batch = RPI * NB < drop ? RPI * NB : drop;
+  for (int r0 = 0; r0 < rows; r0 += batch) {
+    u32x4 buf[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int r = r0 + ro + RPI * k;
+      if (r < r0 + batch && r < rows) buf[k] = ld16(base + (int64_t)(r + drop) * ring.rs + col);
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int r = r0 + ro + RPI * k;
+      if (r < r0 + batch && r < rows) st16(base + (int64_t)r * ring.rs + col, buf[k]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const rkv_cfg* cfg, const rkv_step_plan* plan, const RingArgs& ring,
+                         const uint16_t* knew, const uint16_t* vnew, hipStream_t stream) {
+  const int S = cfg->num_streams, H = cfg->num_kv_heads, L = cfg->num_layers;
+  const dim3 grid(L * S * H, cfg->new_rows);
+  const bool comp = (cfg->flags & RKV_F_COMPENSATED) != 0;
+  const bool enc = cfg->mode == RKV_MODE_ENC_CHUNK;
+  const int F = cfg->new_rows;
+#define RKV_APPEND(DD, CC, EE)                                                                  \
+  hipLaunchKernelGGL((append_kernel<DD, CC, EE>), grid, dim3(64), 0, stream, plan, ring, knew, \
+                     vnew, S, H, F)
+  if (cfg->head_dim == 128) {
+    if (enc) RKV_APPEND(128, false, true);
+    else if (comp) RKV_APPEND(128, true, false);
+    else RKV_APPEND(128, false, false);
+  } else {
+    if (enc) RKV_APPEND(64, false, true);
+    else if (comp) RKV_APPEND(64, true, false);
+    else RKV_APPEND(64, false, false);
+  }
+#undef RKV_APPEND
+  return hipGetLastError();
+}
+
+hipError_t launch_rebase(const rkv_cfg* cfg, const rkv_step_plan* plan, const RingArgs& ring,
+                         hipStream_t stream) {
+  const int S = cfg->num_streams, H = cfg->num_kv_heads, L = cfg->num_layers;
+  const bool comp = (cfg->flags & RKV_F_COMPENSATED) != 0;
+  const int rpb = 256 / (cfg->head_dim / 16);
+  const dim3 grid(L * S * H, (ring.slots + rpb - 1) / rpb);
+  if (cfg->head_dim == 128) {
+    if (comp) hipLaunchKernelGGL((rebase_kernel<128, true>), grid, dim3(256), 0, stream, plan, ring, S, H);
+    else hipLaunchKernelGGL((rebase_kernel<128, false>), grid, dim3(256), 0, stream, plan, ring, S, H);
+  } else {
+    if (comp) hipLaunchKernelGGL((rebase_kernel<64, true>), grid, dim3(256), 0, stream, plan, ring, S, H);
+    else hipLaunchKernelGGL((rebase_kernel<64, false>), grid, dim3(256), 0, stream, plan, ring, S, H);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const rkv_cfg* cfg, const rkv_step_plan* plan, const RingArgs& ring,
+                          hipStream_t stream) {
+  const int S = cfg->num_streams, H = cfg->num_kv_heads, L = cfg->num_layers;
+  const dim3 grid(L * S * H, 4, 2);
+  if (cfg->head_dim == 128)
+    hipLaunchKernelGGL((compact_kernel<128>), grid, dim3(64), 0, stream, plan, ring, S, H);
+  else
+    hipLaunchKernelGGL((compact_kernel<64>), grid, dim3(64), 0, stream, plan, ring, S, H);
+  return hipGetLastError();
+}
+
+}  // namespace rkv

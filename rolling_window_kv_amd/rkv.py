@@ -1,0 +1,296 @@
+"""ctypes binding of librkv.so (declared in include/rkv.h).
+
+Argument marshalling only: torch tensors are passed as device pointers and the
+current torch HIP stream is passed as the stream; every step of the path runs
+in the library's HIP kernels.  There is no fallback: if the library is not
+built, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librkv.so")
+
+RKV_OK = 0
+RKV_EINVAL = -1
+RKV_EUNSUPPORTED = -2
+RKV_EALIGN = -3
+RKV_ESTATE = -4
+RKV_EHIP = -5
+RKV_ESPACE = -6
+
+RKV_MODE_REBASE = 0
+RKV_MODE_COMPACT = 1
+RKV_MODE_ENC_CHUNK = 2
+
+RKV_F_COMPENSATED = 1
+RKV_F_OUT_F32 = 2
+
+RKV_MAX_NEW_ROWS = 8
+RKV_MAX_HEAD_DIM = 128
+
+# Entry points declared in include/rkv.h (checked by the ABI tests).
+ENTRY_POINTS = (
+    "rkv_version", "rkv_strerror", "rkv_last_hip_error", "rkv_validate_cfg",
+    "rkv_state_init_host", "rkv_workspace_bytes", "rkv_advance", "rkv_append",
+    "rkv_roll_rebase", "rkv_compact", "rkv_decode_attn", "rkv_decode_step",
+    "rkv_encoder_chunk_attn",
+)
+
+
+class RkvError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = f"{fn} failed: {status} ({strerror(status)})"
+        if status == RKV_EHIP:
+            msg += f", hipError {lib().rkv_last_hip_error()}"
+        super().__init__(msg)
+        self.status = status
+
+
+class rkv_cfg(ctypes.Structure):
+    _fields_ = [
+        ("num_streams", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("mode", ctypes.c_int32),
+        ("rebase_chunk", ctypes.c_int32), ("new_rows", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("num_splits", ctypes.c_int32),
+        ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class rkv_kv_view(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_lo", ctypes.c_void_p),
+        ("layer_stride", ctypes.c_int64), ("stream_stride", ctypes.c_int64),
+        ("head_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
+        ("slots", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+STATE_DTYPE = np.dtype([
+    ("t", "<i8"), ("origin", "<i8"), ("pos_offset", "<i8"),
+    ("len", "<i4"), ("window", "<i4"), ("cap", "<i4"), ("reserved", "<i4", (3,)),
+])
+
+PLAN_DTYPE = np.dtype([
+    ("t", "<i8"), ("pos", "<i8"), ("pos_offset", "<i8"), ("first_pos", "<i8"),
+    ("evict_pos", "<i8"), ("slot", "<i4"), ("n_valid", "<i4"), ("rebase_delta", "<i4"),
+    ("compact_drop", "<i4"), ("evict_slot", "<i4"), ("window", "<i4"), ("cap", "<i4"),
+    ("new_rows", "<i4"), ("reserved", "<i4", (14,)),
+    ("rope_new", "<f8", (RKV_MAX_NEW_ROWS, 2, RKV_MAX_HEAD_DIM // 2)),
+    ("rope_delta", "<f8", (2, RKV_MAX_HEAD_DIM // 2)),
+])
+assert STATE_DTYPE.itemsize == 48 and PLAN_DTYPE.itemsize == 9344
+
+_lib = None
+
+
+def lib():
+    """The loaded librkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is not built; run `python -m rolling_window_kv_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        pc = ctypes.POINTER(rkv_cfg)
+        pk = ctypes.POINTER(rkv_kv_view)
+        sig = {
+            "rkv_version": ([], ctypes.c_int),
+            "rkv_strerror": ([ctypes.c_int], ctypes.c_char_p),
+            "rkv_last_hip_error": ([], ctypes.c_int),
+            "rkv_validate_cfg": ([pc], ctypes.c_int),
+            "rkv_state_init_host": ([pc, vp, vp, vp, vp], ctypes.c_int),
+            "rkv_workspace_bytes": ([pc, i32], sz),
+            "rkv_advance": ([pc, vp, vp, vp], ctypes.c_int),
+            "rkv_append": ([pc, vp, pk, vp, vp, vp], ctypes.c_int),
+            "rkv_roll_rebase": ([pc, vp, pk, vp], ctypes.c_int),
+            "rkv_compact": ([pc, vp, pk, vp], ctypes.c_int),
+            "rkv_decode_attn": ([pc, vp, pk, vp, vp, vp, sz, vp], ctypes.c_int),
+            "rkv_decode_step": ([pc, vp, pk, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "rkv_encoder_chunk_attn": ([pc, vp, pk, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def make_cfg(num_streams, num_layers, num_q_heads=16, num_kv_heads=2, head_dim=128,
+             mode=RKV_MODE_REBASE, rebase_chunk=1, new_rows=1, flags=0, num_splits=0,
+             rope_base=1e6, softmax_scale=0.0) -> rkv_cfg:
+    return rkv_cfg(num_streams, num_layers, num_q_heads, num_kv_heads, head_dim, mode,
+                   rebase_chunk, new_rows, flags, num_splits, rope_base, softmax_scale, 0)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != RKV_OK:
+        raise RkvError(fn, rc)
+
+
+def kv_view(k, v, k_lo=None) -> rkv_kv_view:
+    """View of cache tensors shaped [L, S, Hkv, slots, d] (bf16, last dim contiguous)."""
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("K and V must have the same shape and strides")
+    if k.stride(-1) != 1:
+        raise ValueError("head_dim must be contiguous")
+    if k_lo is not None and (k_lo.shape != k.shape or k_lo.stride() != k.stride()):
+        raise ValueError("k_lo must match K")
+    st = k.stride()
+    return rkv_kv_view(k.data_ptr(), v.data_ptr(), None if k_lo is None else k_lo.data_ptr(),
+                       st[0], st[1], st[2], st[3], k.shape[3], 0)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def rkv_version() -> int:
+    return lib().rkv_version()
+
+
+def strerror(status) -> str:
+    return lib().rkv_strerror(int(status)).decode()
+
+
+rkv_strerror = strerror
+
+
+def rkv_last_hip_error() -> int:
+    return lib().rkv_last_hip_error()
+
+
+def rkv_validate_cfg(cfg) -> int:
+    return lib().rkv_validate_cfg(ctypes.byref(cfg))
+
+
+def rkv_state_init_host(cfg, window, cap, origin) -> np.ndarray:
+    """Per-stream initial states as a STATE_DTYPE array (host)."""
+    S = cfg.num_streams
+    w = np.ascontiguousarray(np.broadcast_to(np.asarray(window, np.int32), (S,)))
+    c = np.ascontiguousarray(np.broadcast_to(np.asarray(cap, np.int32), (S,)))
+    o = np.ascontiguousarray(np.broadcast_to(np.asarray(origin, np.int64), (S,)))
+    out = np.zeros(S, STATE_DTYPE)
+    rc = lib().rkv_state_init_host(ctypes.byref(cfg), w.ctypes.data, c.ctypes.data,
+                                   o.ctypes.data, out.ctypes.data)
+    _check("rkv_state_init_host", rc)
+    return out
+
+
+def rkv_workspace_bytes(cfg, slots) -> int:
+    return int(lib().rkv_workspace_bytes(ctypes.byref(cfg), int(slots)))
+
+
+def rkv_advance(cfg, state, plan, stream=None):
+    _check("rkv_advance", lib().rkv_advance(ctypes.byref(cfg), _ptr(state), _ptr(plan),
+                                            _stream(stream)))
+
+
+def rkv_append(cfg, plan, kv, k_new, v_new, stream=None):
+    _check("rkv_append", lib().rkv_append(ctypes.byref(cfg), _ptr(plan), ctypes.byref(kv),
+                                          _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+
+def rkv_roll_rebase(cfg, plan, kv, stream=None):
+    _check("rkv_roll_rebase", lib().rkv_roll_rebase(ctypes.byref(cfg), _ptr(plan),
+                                                    ctypes.byref(kv), _stream(stream)))
+
+
+def rkv_compact(cfg, plan, kv, stream=None):
+    _check("rkv_compact", lib().rkv_compact(ctypes.byref(cfg), _ptr(plan), ctypes.byref(kv),
+                                            _stream(stream)))
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def rkv_decode_attn(cfg, plan, kv, q, out, workspace=None, stream=None):
+    wp, wb = _ws(workspace)
+    _check("rkv_decode_attn", lib().rkv_decode_attn(ctypes.byref(cfg), _ptr(plan),
+                                                    ctypes.byref(kv), _ptr(q), _ptr(out),
+                                                    wp, wb, _stream(stream)))
+
+
+def rkv_decode_step(cfg, plan, kv, q, k_new, v_new, out, workspace=None, stream=None):
+    wp, wb = _ws(workspace)
+    _check("rkv_decode_step", lib().rkv_decode_step(ctypes.byref(cfg), _ptr(plan),
+                                                    ctypes.byref(kv), _ptr(q), _ptr(k_new),
+                                                    _ptr(v_new), _ptr(out), wp, wb,
+                                                    _stream(stream)))
+
+
+def rkv_encoder_chunk_attn(cfg, plan, kv, q, k_new, v_new, out, workspace=None, stream=None):
+    wp, wb = _ws(workspace)
+    _check("rkv_encoder_chunk_attn",
+           lib().rkv_encoder_chunk_attn(ctypes.byref(cfg), _ptr(plan), ctypes.byref(kv), _ptr(q),
+                                        _ptr(k_new), _ptr(v_new), _ptr(out), wp, wb,
+                                        _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# device buffers for one cache (torch is only the allocator)
+# ---------------------------------------------------------------------------
+
+class Cache:
+    """Device tensors of one rolling cache: rings, per-stream state, plan, workspace."""
+
+    def __init__(self, cfg, slots, window, cap, origin=0, device="cuda", zero=True):
+        import torch
+        self.cfg = cfg
+        L, S, H, d = cfg.num_layers, cfg.num_streams, cfg.num_kv_heads, cfg.head_dim
+        shape = (L, S, H, slots, d)
+        alloc = torch.zeros if zero else torch.empty
+        self.k = alloc(shape, dtype=torch.bfloat16, device=device)
+        self.v = alloc(shape, dtype=torch.bfloat16, device=device)
+        self.k_lo = (alloc(shape, dtype=torch.bfloat16, device=device)
+                     if cfg.flags & RKV_F_COMPENSATED else None)
+        self.kv = kv_view(self.k, self.v, self.k_lo)
+        host = rkv_state_init_host(cfg, window, cap, origin)
+        self.state = torch.from_numpy(host.view(np.uint8).copy()).to(device)
+        self.plan = torch.zeros(S * PLAN_DTYPE.itemsize, dtype=torch.uint8, device=device)
+        nbytes = rkv_workspace_bytes(cfg, slots)
+        self.workspace = (torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=device)
+                          if nbytes else None)
+
+    def plan_host(self) -> np.ndarray:
+        return self.plan.cpu().numpy().view(PLAN_DTYPE)
+
+    def state_host(self) -> np.ndarray:
+        return self.state.cpu().numpy().view(STATE_DTYPE)
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)

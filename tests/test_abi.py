@@ -1,0 +1,186 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/rkv.h declares, struct layouts agree with the binding, and host-side
+validation rejects bad arguments before any HIP call (fake pointers used here
+always fail validation, so nothing is ever launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import schedule as sch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rkv.h")
+
+
+@pytest.fixture(scope="module")
+def rkv():
+    from rolling_window_kv_amd import rkv as mod
+    if not os.path.exists(mod.lib_path()):
+        from rolling_window_kv_amd import build
+        build.build()
+    mod.lib()
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(rkv_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_entry_points(rkv):
+    assert declared_functions() == sorted(rkv.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol(rkv):
+    out = subprocess.run(["nm", "-D", "--defined-only", rkv.lib_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(rkv.lib(), name) is not None
+
+
+def test_struct_sizes(rkv):
+    assert ctypes.sizeof(rkv.rkv_cfg) == 56
+    assert ctypes.sizeof(rkv.rkv_kv_view) == 64
+    assert rkv.STATE_DTYPE.itemsize == 48
+    assert rkv.PLAN_DTYPE.itemsize == 9344
+
+
+def test_version_and_strerror(rkv):
+    assert rkv.rkv_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert isinstance(rkv.strerror(code), str) and rkv.strerror(code)
+    assert rkv.rkv_last_hip_error() == 0
+
+
+def good_cfg(rkv, **kw):
+    base = dict(num_streams=4, num_layers=2, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                mode=rkv.RKV_MODE_REBASE, rebase_chunk=25)
+    base.update(kw)
+    return rkv.make_cfg(**base)
+
+
+def test_cfg_validation(rkv):
+    assert rkv.rkv_validate_cfg(good_cfg(rkv)) == 0
+    bad = [
+        (dict(num_streams=0), rkv.RKV_EINVAL),
+        (dict(head_dim=96), rkv.RKV_EUNSUPPORTED),
+        (dict(num_q_heads=15), rkv.RKV_EINVAL),
+        (dict(num_q_heads=32, num_kv_heads=2), rkv.RKV_EUNSUPPORTED),
+        (dict(rebase_chunk=0), rkv.RKV_EINVAL),
+        (dict(mode=7), rkv.RKV_EUNSUPPORTED),
+        (dict(flags=8), rkv.RKV_EUNSUPPORTED),
+        (dict(rope_base=-1.0), rkv.RKV_EINVAL),
+        (dict(rope_base=float("inf")), rkv.RKV_EINVAL),
+        (dict(softmax_scale=-1.0), rkv.RKV_EINVAL),
+        (dict(new_rows=2), rkv.RKV_EINVAL),
+        (dict(mode=rkv.RKV_MODE_COMPACT, flags=rkv.RKV_F_COMPENSATED), rkv.RKV_EUNSUPPORTED),
+        (dict(mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=4), rkv.RKV_EINVAL),       # Hq != Hkv
+        (dict(mode=rkv.RKV_MODE_ENC_CHUNK, num_q_heads=20, num_kv_heads=20, head_dim=64,
+              new_rows=9), rkv.RKV_EUNSUPPORTED),
+    ]
+    for kw, code in bad:
+        assert rkv.rkv_validate_cfg(good_cfg(rkv, **kw)) == code, kw
+    enc = good_cfg(rkv, mode=rkv.RKV_MODE_ENC_CHUNK, num_q_heads=20, num_kv_heads=20,
+                   head_dim=64, new_rows=4)
+    assert rkv.rkv_validate_cfg(enc) == 0
+
+
+@pytest.mark.parametrize("mode,W,cap,dc,F", [(0, 375, 375, 25, 1), (0, 188, 188, 1, 1),
+                                              (1, 8192, 9216, 1, 1), (2, 750, 754, 1, 4)])
+def test_state_init_matches_oracle(rkv, mode, W, cap, dc, F):
+    kw = dict(mode=mode, rebase_chunk=dc, new_rows=F)
+    if mode == 2:
+        kw.update(num_q_heads=20, num_kv_heads=20, head_dim=64)
+    cfg = good_cfg(rkv, **kw)
+    origins = np.array([0, 1, 4321, 5000], np.int64)
+    st = rkv.rkv_state_init_host(cfg, W, cap, origins)
+    for s in range(4):
+        ref = sch.init_state(mode, W, cap, int(origins[s]), dc, F)
+        assert (st["t"][s], st["origin"][s], st["pos_offset"][s], st["len"][s],
+                st["window"][s], st["cap"][s]) == (ref.t, ref.origin, ref.pos_offset,
+                                                    ref.length, ref.window, ref.cap)
+
+
+def test_state_init_rejects_inconsistent_streams(rkv):
+    cfg = good_cfg(rkv)
+    with pytest.raises(rkv.RkvError) as e:
+        rkv.rkv_state_init_host(cfg, 375, 376, 0)
+    assert e.value.status == rkv.RKV_ESTATE
+    with pytest.raises(rkv.RkvError):
+        rkv.rkv_state_init_host(cfg, 375, 375, -1)
+    ccfg = good_cfg(rkv, mode=rkv.RKV_MODE_COMPACT)
+    with pytest.raises(rkv.RkvError):
+        rkv.rkv_state_init_host(ccfg, 8192, 8192, 0)
+    ecfg = good_cfg(rkv, mode=rkv.RKV_MODE_ENC_CHUNK, num_q_heads=20, num_kv_heads=20,
+                    head_dim=64, new_rows=4)
+    with pytest.raises(rkv.RkvError):
+        rkv.rkv_state_init_host(ecfg, 750, 753, 0)
+
+
+def test_workspace_sizes(rkv):
+    # 36 x 64 x 2 = 4608 items: no split needed
+    assert rkv.rkv_workspace_bytes(good_cfg(rkv, num_streams=64, num_layers=36), 375) == 0
+    # one stream, one layer: split into ceil(375/64) = 6 ranges
+    ws = rkv.rkv_workspace_bytes(good_cfg(rkv, num_streams=1, num_layers=1, rebase_chunk=1), 375)
+    assert ws == 2 * 6 * (16 + 8 * 128) * 4
+    assert rkv.rkv_workspace_bytes(good_cfg(rkv, head_dim=3), 375) == 0
+
+
+FAKE = 0x10000           # never dereferenced: every call below fails validation
+MISALIGNED = 0x10008
+
+
+def fake_view(rkv, k=FAKE, lo=None, slot_stride=128, slots=375):
+    return rkv.rkv_kv_view(k, FAKE, lo, 2 * 4 * 375 * 128 * 0 + 4 * 2 * 375 * 128,
+                           2 * 375 * 128, 375 * 128, slot_stride, slots, 0)
+
+
+def call(rkv, name, *args):
+    return getattr(rkv.lib(), name)(*args)
+
+
+def test_calls_reject_bad_arguments_without_a_device(rkv):
+    cfg = good_cfg(rkv)
+    c = ctypes.byref(cfg)
+    kv = fake_view(rkv)
+    F = ctypes.c_void_p(FAKE)
+    N = None
+    M = ctypes.c_void_p(MISALIGNED)
+    assert call(rkv, "rkv_advance", c, N, F, N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_advance", N, F, F, N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_append", c, F, ctypes.byref(kv), N, F, N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_append", c, F, ctypes.byref(kv), M, F, N) == rkv.RKV_EALIGN
+    assert call(rkv, "rkv_append", c, F, N, F, F, N) == rkv.RKV_EINVAL
+    bad_stride = fake_view(rkv, slot_stride=100)
+    assert call(rkv, "rkv_roll_rebase", c, F, ctypes.byref(bad_stride), N) == rkv.RKV_EINVAL
+    odd_stride = fake_view(rkv, slot_stride=132)
+    assert call(rkv, "rkv_roll_rebase", c, F, ctypes.byref(odd_stride), N) == rkv.RKV_EALIGN
+    mis = fake_view(rkv, k=MISALIGNED)
+    assert call(rkv, "rkv_roll_rebase", c, F, ctypes.byref(mis), N) == rkv.RKV_EALIGN
+    assert call(rkv, "rkv_roll_rebase", c, N, ctypes.byref(kv), N) == rkv.RKV_EINVAL
+    # mode mismatches
+    assert call(rkv, "rkv_compact", c, F, ctypes.byref(kv), N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_encoder_chunk_attn", c, F, ctypes.byref(kv), F, F, F, F, N, 0,
+                N) == rkv.RKV_EINVAL
+    # compensated needs k_lo
+    ccfg = good_cfg(rkv, flags=rkv.RKV_F_COMPENSATED)
+    assert call(rkv, "rkv_roll_rebase", ctypes.byref(ccfg), F, ctypes.byref(kv),
+                N) == rkv.RKV_EINVAL
+    # decode: missing workspace when the key range is split
+    one = good_cfg(rkv, num_streams=1, num_layers=1)
+    assert call(rkv, "rkv_decode_attn", ctypes.byref(one), F, ctypes.byref(kv), F, F, N, 0,
+                N) == rkv.RKV_ESPACE
+    assert call(rkv, "rkv_decode_step", ctypes.byref(one), F, ctypes.byref(kv), F, F, F, F,
+                F, 16, N) == rkv.RKV_ESPACE
+    assert call(rkv, "rkv_decode_attn", c, F, ctypes.byref(kv), M, F, N, 0,
+                N) == rkv.RKV_EALIGN
+    assert call(rkv, "rkv_decode_step", c, F, ctypes.byref(kv), F, F, N, F, N, 0,
+                N) == rkv.RKV_EINVAL
+    assert rkv.rkv_last_hip_error() == 0
