@@ -1,10 +1,11 @@
 // Windowed attention over the rolling cache on gfx950 matrix cores.
 //
-// One workgroup handles one (layer, stream, kv head) item -- or one split of
-// its key range -- with NW waves that take 16-key tiles in turn, each wave
-// loading its next tile while it computes the current one.  The G query
-// vectors that share the KV head (the 8 query heads of a GQA group, or the F
-// frames of an encoder chunk) form the N side of the matrix-core products:
+// One workgroup of NW waves handles one (layer, stream, kv head) item -- or
+// one split of its key range.  The waves take 16-key tiles in turn, each
+// loading its next tile while it computes the current one, and merge their
+// partial softmax states through LDS at the end.  The G query vectors that
+// share the KV head (the 8 query heads of a GQA group, or the F frames of an
+// encoder chunk) form the N side of the matrix-core products:
 //
 //   scores  S[key][col] = K[key][:] . Qt[:][col]   v_mfma_f32_16x16x32_bf16
 //   output  O[d][col]  += Vt[d][key] . P[key][col]  v_mfma_f32_16x16x16_bf16
@@ -22,20 +23,21 @@
 // 16x16x16 probability MFMA (k = 4*g4 .. 4*g4+3).  V rows key0 + 4*g4 + j
 // (j < 4) are loaded row-contiguously (lane reads dims CW*c .. CW*c+CW-1, so
 // each load instruction covers four whole rows) and transposed in registers
-// into the A operand (row c <-> dim CW*c + e for product e).  Output lane
-// (g4, c < 8) ends with dims [4*CW*g4, 4*CW*g4 + 4*CW) of query column c.
+// (v_perm) into the A operand (row c <-> dim CW*c + e for product e).  Output
+// lane (g4, c < 8) ends with dims [4*CW*g4, 4*CW*g4 + 4*CW) of column c.
 //
-// Softmax is online with a lazily moved maximum: probabilities use the
-// running maximum m until a tile's maximum exceeds it by more than 2^8 (in
-// log2 units), so rescaling of the accumulators is rare; the result is the
-// same softmax.
+// The rotated query is built once per workgroup (the waves split the rotary
+// pairs) and shared through LDS.  Softmax is online with a lazily moved
+// maximum: probabilities use the running maximum m until a tile's maximum
+// exceeds it by more than 2^8 (log2 units), so accumulator rescaling is rare.
 //
 // The fused kinds also update the cache in the same launch, with results
 // identical to running rkv_roll_rebase, rkv_append and the read-only kind in
 // turn: before its attention loop each wave rotates the new row(s) of its
 // tiles from k_new in float64 and writes them (RoPE-on-append), and in REBASE
 // mode, when the plan's delta D > 0, rotates every other retained row of its
-// tiles by R(-D) in float64 and writes it back (exact re-base).
+// tiles by R(-D) in float64 and writes it back (exact re-base).  The attention
+// loop then reads those rows back; each tile is owned by one wave.
 
 #include "rkv_device.h"
 #include "rkv_internal.h"
@@ -51,6 +53,14 @@ __device__ __forceinline__ float dpp_ror8(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// low / high bfloat16 halves of two words, packed: {a.lo, b.lo} or {a.hi, b.hi}
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
 template <int CW>
 struct VChunk;
 template <>
@@ -59,9 +69,6 @@ struct VChunk<8> {
   static __device__ __forceinline__ T load(const uint16_t* p) { return ld16(p); }
   static __device__ __forceinline__ void store(uint16_t* p, const T& w) { st16(p, w); }
   static __device__ __forceinline__ T zero() { return u32x4{0u, 0u, 0u, 0u}; }
-  static __device__ __forceinline__ uint32_t elem(const T& w, int e) {
-    return (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-  }
 };
 template <>
 struct VChunk<4> {
@@ -69,9 +76,6 @@ struct VChunk<4> {
   static __device__ __forceinline__ T load(const uint16_t* p) { return ld8(p); }
   static __device__ __forceinline__ void store(uint16_t* p, const T& w) { st8(p, w); }
   static __device__ __forceinline__ T zero() { return u32x2{0u, 0u}; }
-  static __device__ __forceinline__ uint32_t elem(const T& w, int e) {
-    return (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-  }
 };
 
 constexpr float kLazyMax = 8.0f;  // rescale only when the max grows by > 2^8
@@ -94,9 +98,10 @@ void attn_kernel(AttnArgs a) {
   typedef VChunk<CW> VC;
   typedef typename VC::T VT;
 
+  __shared__ u32x4 sm_q[KS][64];
   __shared__ float sm_m[NW][8];
   __shared__ float sm_l[NW][8];
-  __shared__ float sm_o[NW][8][D];
+  __shared__ float sm_o[NW > 1 ? NW - 1 : 1][8][D];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -115,7 +120,8 @@ void attn_kernel(AttnArgs a) {
   const int slots = a.ring.slots;
   const int per = (((slots + a.nsplit - 1) / a.nsplit) + TK - 1) & ~(TK - 1);
   const int kb = split * per;
-  const int kalloc = kb + per < slots ? kb + per : slots;
+  const int n_valid = P->n_valid < slots ? P->n_valid : slots;
+  const int ke = kb + per < n_valid ? kb + per : n_valid;
 
   const int64_t rbase = (int64_t)l * a.ring.ls + (int64_t)s * a.ring.ss + (int64_t)g * a.ring.hs;
   uint16_t* __restrict__ Kp = a.ring.k + rbase;
@@ -135,11 +141,155 @@ void attn_kernel(AttnArgs a) {
     return (((int64_t)l * a.S + s) * a.Hkv + g) * D;
   };
 
-  // ---- tile loads (rows clamped into the allocation; masked later) ----
+  // ---- rotated query, split into hi/lo bfloat16 columns, built once ----
+  {
+    const bool has = col_q < a.G;
+    const uint16_t* qp = a.q + vec_off(has ? col_q : 0);
+    const int rrow = (KIND == kEncoderFused) ? col_q : 0;
+    for (int st = wave; st < KH; st += NW) {
+      const u32x4 x1 = has ? ld16(qp + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 x2 = has ? ld16(qp + 32 * (st + KH) + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
+      const double* cs = P->rope_new[rrow][0] + 32 * st + 8 * g4;
+      const double* sn = P->rope_new[rrow][1] + 32 * st + 8 * g4;
+      u32x4 w1, w2;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float y1[2], y2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = 2 * w + h;
+          const float a1 = bf2f(elem8(x1, e)), a2 = bf2f(elem8(x2, e));
+          const float cq = (float)cs[e], sq = (float)sn[e];
+          y1[h] = fmaf(a1, cq, -(a2 * sq));
+          y2[h] = fmaf(a1, sq, a2 * cq);
+        }
+        const uint32_t h1 = cvt2_bf16(y1[0], y1[1]);
+        const uint32_t h2 = cvt2_bf16(y2[0], y2[1]);
+        if (part) {
+          w1[w] = cvt2_bf16(y1[0] - bf2f(h1 & 0xffffu), y1[1] - bf2f(h1 >> 16));
+          w2[w] = cvt2_bf16(y2[0] - bf2f(h2 & 0xffffu), y2[1] - bf2f(h2 >> 16));
+        } else {
+          w1[w] = h1;
+          w2[w] = h2;
+        }
+      }
+      sm_q[st][lane] = w1;
+      sm_q[st + KH][lane] = w2;
+    }
+  }
+
+  // ---- fused-update parameters ----
+  const int delta = (KIND == kDecodeFused) ? P->rebase_delta : 0;
+  const int slot_new = P->slot;
+  const int nnew = P->new_rows;
+  const int cap = P->cap;
+
+  auto new_index = [&](int row) -> int {
+    if (KIND == kDecodeFused) return row == slot_new ? 0 : -1;
+    const int dj = (row - slot_new + cap) % cap;
+    return dj < nnew ? dj : -1;
+  };
+
+  // Rotate this lane's K chunks of one row in float64, store them correctly
+  // rounded; pairs are chunks (st, st + KH).  src: chunks to rotate (k_new or
+  // the stored row); lo: stored residual (compensated re-base); sgn = -1
+  // rotates by the negative angle.
+  auto rotate_row = [&](const u32x4* src, const u32x4* lo, const double* cs, const double* sn,
+                        double sgn, int row) {
+#pragma unroll
+    for (int st = 0; st < KH; ++st) {
+      u32x4 w1, w2, r1, r2;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        double y1[2], y2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = 2 * w + h;
+          const int i = 32 * st + 8 * g4 + e;
+          double x1 = bf2f(elem8(src[st], e)), x2 = bf2f(elem8(src[st + KH], e));
+          if (COMP && lo) {
+            x1 += (double)bf2f(elem8(lo[st], e));
+            x2 += (double)bf2f(elem8(lo[st + KH], e));
+          }
+          rotate_pair64(x1, x2, cs[i], sgn * sn[i], y1[h], y2[h]);
+        }
+        w1[w] = cvt2_bf16_f64(y1[0], y1[1]);
+        w2[w] = cvt2_bf16_f64(y2[0], y2[1]);
+        if (COMP) {
+          r1[w] = cvt2_bf16_f64(y1[0] - (double)bf2f(w1[w] & 0xffffu),
+                                y1[1] - (double)bf2f(w1[w] >> 16));
+          r2[w] = cvt2_bf16_f64(y2[0] - (double)bf2f(w2[w] & 0xffffu),
+                                y2[1] - (double)bf2f(w2[w] >> 16));
+        }
+      }
+      st16(Kp + row * rs + 32 * st + 8 * g4, w1);
+      st16(Kp + row * rs + 32 * (st + KH) + 8 * g4, w2);
+      if (COMP) {
+        st16(Lp + row * rs + 32 * st + 8 * g4, r1);
+        st16(Lp + row * rs + 32 * (st + KH) + 8 * g4, r2);
+      }
+    }
+  };
+
+  // ---- fused cache updates: a pre-pass over this wave's own tiles ----
+  if (KIND != kDecodeRead) {
+    for (int tt = wave;; tt += NW) {
+      const int key0 = kb + TK * tt;
+      if (key0 >= ke) break;
+      bool any_new = true;
+      if (KIND == kDecodeFused) any_new = slot_new >= key0 && slot_new < key0 + TK;
+      if (delta == 0 && !any_new) continue;
+      const int row = key0 + c;
+      if (row < ke) {
+        const int jn = new_index(row);
+        if (jn >= 0) {
+          u32x4 src[KS];
+          const uint16_t* kn = a.knew + new_off(jn);
+#pragma unroll
+          for (int st = 0; st < KS; ++st) src[st] = ld16(kn + 32 * st + 8 * g4);
+          rotate_row(src, nullptr, P->rope_new[jn][0], P->rope_new[jn][1], 1.0, row);
+        } else if (delta != 0) {
+          u32x4 src[KS], lo[KS];
+#pragma unroll
+          for (int st = 0; st < KS; ++st) {
+            src[st] = ld16(Kp + row * rs + 32 * st + 8 * g4);
+            lo[st] = COMP ? ld16(Lp + row * rs + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
+          }
+          rotate_row(src, COMP ? lo : nullptr, P->rope_delta[0], P->rope_delta[1], -1.0, row);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rv = key0 + 4 * g4 + j;
+        if (rv >= ke) continue;
+        const int jn = new_index(rv);
+        if (jn >= 0) VC::store(Vp + rv * rs + CW * c, VC::load(a.vnew + new_off(jn) + CW * c));
+      }
+    }
+  }
+
+  __syncthreads();  // the query operand is in LDS
+  bf16x8 qop[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) qop[st] = __builtin_bit_cast(bf16x8, sm_q[st][lane]);
+
+  // encoder mask bookkeeping
+  const int64_t last_pos = P->t;
+  const int slot_last = (slot_new + nnew - 1) % cap;
+  const int64_t first_pos = P->first_pos;
+  const int64_t qpos = P->pos + col_q;
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4 oacc[CW];
+#pragma unroll
+  for (int e = 0; e < CW; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   struct Tile {
     u32x4 k[KS];
     VT v[4];
   };
+  // rows clamped into the allocation (masked rows are never used)
   auto load_tile = [&](int key0, Tile& T) {
     const int rk = key0 + c < slots ? key0 + c : slots - 1;
 #pragma unroll
@@ -152,139 +302,28 @@ void attn_kernel(AttnArgs a) {
     }
   };
 
-  // The first tile is requested before the plan is read.
-  Tile t0, t1;
-  int tile = wave;
-  if (kb + TK * tile < kalloc) load_tile(kb + TK * tile, t0);
-
-  const int n_valid = P->n_valid < slots ? P->n_valid : slots;
-  const int ke = kb + per < n_valid ? kb + per : n_valid;
-
-  // ---- rotated query, split into hi/lo bfloat16 columns (B operand) ----
-  bf16x8 qop[KS];
-  {
-    const bool has = col_q < a.G;
-    const uint16_t* qp = a.q + vec_off(has ? col_q : 0);
-    const int rrow = (KIND == kEncoderFused) ? col_q : 0;
-    u32x4 qraw[KS];
-#pragma unroll
-    for (int st = 0; st < KS; ++st)
-      qraw[st] = has ? ld16(qp + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int st = 0; st < KH; ++st) {
-      u32x4 w1, w2;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t o1 = 0, o2 = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int e = 2 * w + h;
-          const int i = 32 * st + 8 * g4 + e;
-          double y1, y2;
-          rotate_pair64(bf2f(elem8(qraw[st], e)), bf2f(elem8(qraw[st + KH], e)),
-                        P->rope_new[rrow][0][i], P->rope_new[rrow][1][i], y1, y2);
-          const uint32_t h1 = f64_to_bf16(y1), h2 = f64_to_bf16(y2);
-          const uint32_t b1 = part ? f64_to_bf16(y1 - (double)bf2f(h1)) : h1;
-          const uint32_t b2 = part ? f64_to_bf16(y2 - (double)bf2f(h2)) : h2;
-          o1 |= b1 << (16 * h);
-          o2 |= b2 << (16 * h);
-        }
-        w1[w] = o1;
-        w2[w] = o2;
-      }
-      qop[st] = __builtin_bit_cast(bf16x8, w1);
-      qop[st + KH] = __builtin_bit_cast(bf16x8, w2);
-    }
-  }
-
-  // ---- fused-update parameters ----
-  const int delta = (KIND == kDecodeFused) ? P->rebase_delta : 0;
-  const int slot_new = P->slot;
-  const int nnew = P->new_rows;
-  const int cap = P->cap;
-  const int64_t last_pos = P->t;                      // encoder mask bookkeeping
-  const int slot_last = (slot_new + nnew - 1) % cap;
-  const int64_t first_pos = P->first_pos;
-  const int64_t qpos = P->pos + col_q;
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4 oacc[CW];
-#pragma unroll
-  for (int e = 0; e < CW; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto new_index = [&](int row) -> int {
-    if (KIND == kDecodeFused) return row == slot_new ? 0 : -1;
-    const int dj = (row - slot_new + cap) % cap;
-    return dj < nnew ? dj : -1;
-  };
-
-  // Rotate this lane's K chunks of one row in float64 and store them; pairs
-  // are chunks (st, st + KH).  src: chunks to rotate (k_new or the stored
-  // row); lo: stored residual (compensated re-base); sgn = -1 rotates by -angle.
-  auto rotate_row = [&](u32x4* kk, const u32x4* src, const u32x4* lo, const double* cs,
-                        const double* sn, double sgn, int row) {
-#pragma unroll
-    for (int st = 0; st < KH; ++st) {
-      u32x4 w1, w2, r1, r2;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t o1 = 0, o2 = 0, p1 = 0, p2 = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int e = 2 * w + h;
-          const int i = 32 * st + 8 * g4 + e;
-          double x1 = bf2f(elem8(src[st], e)), x2 = bf2f(elem8(src[st + KH], e));
-          if (COMP && lo) {
-            x1 += (double)bf2f(elem8(lo[st], e));
-            x2 += (double)bf2f(elem8(lo[st + KH], e));
-          }
-          double y1, y2;
-          rotate_pair64(x1, x2, cs[i], sgn * sn[i], y1, y2);
-          const uint32_t h1 = f64_to_bf16(y1), h2 = f64_to_bf16(y2);
-          o1 |= h1 << (16 * h);
-          o2 |= h2 << (16 * h);
-          if (COMP) {
-            p1 |= f64_to_bf16(y1 - (double)bf2f(h1)) << (16 * h);
-            p2 |= f64_to_bf16(y2 - (double)bf2f(h2)) << (16 * h);
-          }
-        }
-        w1[w] = o1;
-        w2[w] = o2;
-        r1[w] = p1;
-        r2[w] = p2;
-      }
-      kk[st] = w1;
-      kk[st + KH] = w2;
-      st16(Kp + row * rs + 32 * st + 8 * g4, w1);
-      st16(Kp + row * rs + 32 * (st + KH) + 8 * g4, w2);
-      if (COMP) {
-        st16(Lp + row * rs + 32 * st + 8 * g4, r1);
-        st16(Lp + row * rs + 32 * (st + KH) + 8 * g4, r2);
-      }
-    }
-  };
-
   auto process = [&](Tile& T, int key0) {
-    // ---- scores ----
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < KS; ++st)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[st]), qop[st],
                                                     acc, 0, 0, 0);
+    const bool full = (KIND != kEncoderFused) && key0 + TK <= ke;
     float sv[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x = (acc[r] + dpp_ror8(acc[r])) * a.scale_log2;
-      const int row = key0 + 4 * g4 + r;
-      bool vis = row < ke;
-      if (KIND == kEncoderFused) {
-        const int back = (slot_last - row + cap) % cap;
-        const int64_t kpos = last_pos - back;
-        vis = vis && kpos >= first_pos && kpos <= qpos;
+      if (!full) {
+        const int row = key0 + 4 * g4 + r;
+        bool vis = row < ke;
+        if (KIND == kEncoderFused) {
+          const int back = (slot_last - row + cap) % cap;
+          const int64_t kpos = last_pos - back;
+          vis = vis && kpos >= first_pos && kpos <= qpos;
+        }
+        x = vis ? x : -INFINITY;
       }
-      x = vis ? x : -INFINITY;
       sv[r] = x;
       mx = fmaxf(mx, x);
     }
@@ -299,83 +338,41 @@ void attn_kernel(AttnArgs a) {
       for (int e = 0; e < CW; ++e) oacc[e] *= alpha;
     }
     float pj[4];
+    if (full) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pj[r] = m_run == -INFINITY ? 0.f : fast_exp2(sv[r] - m_run);
-    l_run += (pj[0] + pj[1]) + (pj[2] + pj[3]);
-    uint32_t pw[2];
+      for (int r = 0; r < 4; ++r) pj[r] = fast_exp2(sv[r] - m_run);
+    } else {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t b[2];
+      for (int r = 0; r < 4; ++r) pj[r] = m_run == -INFINITY ? 0.f : fast_exp2(sv[r] - m_run);
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const float p = pj[2 * h + q2];
-        const uint32_t hi = f2bf(p);
-        b[q2] = part ? f2bf(p - bf2f(hi)) : hi;
-      }
-      pw[h] = b[0] | (b[1] << 16);
+      for (int j = 0; j < 4; ++j)
+        if (key0 + 4 * g4 + j >= ke) T.v[j] = VC::zero();
     }
-    const s16x4 pop = __builtin_bit_cast(s16x4, u32x2{pw[0], pw[1]});
+    l_run += (pj[0] + pj[1]) + (pj[2] + pj[3]);
+    const uint32_t h01 = cvt2_bf16(pj[0], pj[1]);
+    const uint32_t h23 = cvt2_bf16(pj[2], pj[3]);
+    uint32_t p01 = h01, p23 = h23;
+    if (part) {
+      p01 = cvt2_bf16(pj[0] - bf2f(h01 & 0xffffu), pj[1] - bf2f(h01 >> 16));
+      p23 = cvt2_bf16(pj[2] - bf2f(h23 & 0xffffu), pj[3] - bf2f(h23 >> 16));
+    }
+    const s16x4 pop = __builtin_bit_cast(s16x4, u32x2{p01, p23});
 
-    // ---- V^T operand (register transpose) and output accumulation ----
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (key0 + 4 * g4 + j >= ke) T.v[j] = VC::zero();
+    // V^T operand: dims CW*c + e of the tile's 4 keys of this lane group
 #pragma unroll
     for (int e = 0; e < CW; ++e) {
-      const uint32_t w0 = VC::elem(T.v[0], e) | (VC::elem(T.v[1], e) << 16);
-      const uint32_t w1 = VC::elem(T.v[2], e) | (VC::elem(T.v[3], e) << 16);
+      const int wd = e >> 1;
+      const uint32_t w0 = (e & 1) ? pack_hi(T.v[0][wd], T.v[1][wd]) : pack_lo(T.v[0][wd], T.v[1][wd]);
+      const uint32_t w1 = (e & 1) ? pack_hi(T.v[2][wd], T.v[3][wd]) : pack_lo(T.v[2][wd], T.v[3][wd]);
       oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{w0, w1}),
                                                            pop, oacc[e], 0, 0, 0);
     }
   };
 
-  // ---- fused cache updates: a pre-pass over this wave's own tiles ----
-  // Re-base (every retained row of the wave's tiles) and append (the new
-  // rows) are written before the attention loop; the loop then reads the
-  // updated rows back.  Tiles are owned by one wave, so no barrier is needed.
-  if (KIND != kDecodeRead) {
-    bool touched_first = false;
-    for (int tt = wave;; tt += NW) {
-      const int key0 = kb + TK * tt;
-      if (key0 >= ke) break;
-      bool any_new = false;
-      if (KIND == kDecodeFused) any_new = slot_new >= key0 && slot_new < key0 + TK;
-      else any_new = true;
-      if (delta == 0 && !any_new) continue;
-      if (tt == wave) touched_first = true;
-      const int row = key0 + c;
-      if (row < ke) {
-        const int jn = new_index(row);
-        if (jn >= 0) {
-          u32x4 src[KS], kk[KS];
-          const uint16_t* kn = a.knew + new_off(jn);
-#pragma unroll
-          for (int st = 0; st < KS; ++st) src[st] = ld16(kn + 32 * st + 8 * g4);
-          rotate_row(kk, src, nullptr, P->rope_new[jn][0], P->rope_new[jn][1], 1.0, row);
-        } else if (delta != 0) {
-          u32x4 src[KS], lo[KS], kk[KS];
-#pragma unroll
-          for (int st = 0; st < KS; ++st) {
-            src[st] = ld16(Kp + row * rs + 32 * st + 8 * g4);
-            lo[st] = COMP ? ld16(Lp + row * rs + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
-          }
-          rotate_row(kk, src, COMP ? lo : nullptr, P->rope_delta[0], P->rope_delta[1], -1.0,
-                     row);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rv = key0 + 4 * g4 + j;
-        if (rv >= ke) continue;
-        const int jn = new_index(rv);
-        if (jn >= 0) VC::store(Vp + rv * rs + CW * c, VC::load(a.vnew + new_off(jn) + CW * c));
-      }
-    }
-    // the early request of the first tile predates these stores
-    if (touched_first) load_tile(kb + TK * wave, t0);
-  }
-
   // ---- main loop: two tiles in registers, the next one loading ----
+  Tile t0, t1;
+  int tile = wave;
+  if (kb + TK * tile < ke) load_tile(kb + TK * tile, t0);
   for (;;) {
     const int key0 = kb + TK * tile;
     if (key0 >= ke) break;
@@ -399,49 +396,82 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) oacc[e][r] += dpp_ror8(oacc[e][r]);
 
-  if (c < 8) {
-    if (g4 == 0) {
-      sm_m[wave][c] = m_run;
-      sm_l[wave][c] = l_run;
+  // ---- merge the waves in wave 0 ----
+  if (NW > 1) {
+    if (wave > 0 && c < 8) {
+      if (g4 == 0) {
+        sm_m[wave][c] = m_run;
+        sm_l[wave][c] = l_run;
+      }
+#pragma unroll
+      for (int e = 0; e < CW; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm_o[wave - 1][c][CW * (4 * g4 + r) + e] = oacc[e][r];
     }
+    __syncthreads();
+    if (wave > 0) return;
+    if (c < 8) {
+      float M = m_run;
 #pragma unroll
-    for (int e = 0; e < CW; ++e)
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][c]);
+      const float f0 = (M == -INFINITY || m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
+      l_run *= f0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm_o[wave][c][CW * (4 * g4 + r) + e] = oacc[e][r];
+      for (int e = 0; e < CW; ++e) oacc[e] *= f0;
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        const float mw = sm_m[w][c];
+        const float fw = (M == -INFINITY || mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+        l_run += fw * sm_l[w][c];
+#pragma unroll
+        for (int e = 0; e < CW; ++e)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[e][r] += fw * sm_o[w - 1][c][CW * (4 * g4 + r) + e];
+      }
+      m_run = M;
+    }
   }
-  __syncthreads();
+  if (c >= 8) return;
 
-  // ---- merge waves; write output or split partial ----
-  const int total = a.G * D;
-  for (int idx = threadIdx.x; idx < total; idx += NW * 64) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float M = -INFINITY;
+  // ---- output (or split partial): dims [4*CW*g4, 4*CW*g4 + 4*CW) of column c ----
+  const int h = c;
+  if (h >= a.G) return;
+  float o[4 * CW];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = sm_m[w][h];
-        const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-        num += f * sm_o[w][h][d];
-        den += f * sm_l[w][h];
-      }
-    }
-    if (a.nsplit == 1) {
-      const float o = den > 0.f ? num / den : 0.f;
-      const int64_t off = vec_off(h) + d;
-      if (a.out_f32) reinterpret_cast<float*>(a.out)[off] = o;
-      else reinterpret_cast<uint16_t*>(a.out)[off] = (uint16_t)f2bf(o);
+    for (int e = 0; e < CW; ++e) o[CW * r + e] = oacc[e][r];
+  const int d0 = 4 * CW * g4;
+  if (a.nsplit == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const int64_t off = vec_off(h) + d0;
+    if (a.out_f32) {
+      float* op = reinterpret_cast<float*>(a.out) + off;
+#pragma unroll
+      for (int q4 = 0; q4 < CW; ++q4)
+        *reinterpret_cast<f32x4*>(op + 4 * q4) =
+            f32x4{o[4 * q4] * inv, o[4 * q4 + 1] * inv, o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv};
     } else {
-      float* pp = a.ws + ((int64_t)item * a.nsplit + split) * partial_floats(D);
-      if (d == 0) {
-        pp[h] = M;
-        pp[8 + h] = den;
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + off;
+#pragma unroll
+      for (int q8 = 0; q8 < CW / 2; ++q8) {
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          w[k] = cvt2_bf16(o[8 * q8 + 2 * k] * inv, o[8 * q8 + 2 * k + 1] * inv);
+        st16(op + 8 * q8, w);
       }
-      pp[16 + h * D + d] = num;
     }
+  } else {
+    float* pp = a.ws + ((int64_t)item * a.nsplit + split) * partial_floats(D);
+    if (g4 == 0) {
+      pp[h] = m_run;
+      pp[8 + h] = l_run;
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < CW; ++q4)
+      *reinterpret_cast<f32x4*>(pp + 16 + h * D + d0 + 4 * q4) =
+          f32x4{o[4 * q4], o[4 * q4 + 1], o[4 * q4 + 2], o[4 * q4 + 3]};
   }
 }
 
@@ -478,7 +508,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   }
 }
 
-constexpr int kWavesPerGroup = 4;
+constexpr int kWavesPerGroup = 2;
 
 template <int D, int KIND, bool COMP>
 hipError_t launch_kind(const AttnArgs& args, int items, hipStream_t stream) {

@@ -29,14 +29,37 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 
 __device__ __forceinline__ float rne_bf16f(float f) { return bf2f(f2bf(f)); }
 
-// float64 -> bfloat16 bit pattern, correctly rounded to nearest even: round
-// to float32 toward zero and set the last bit when inexact (round to odd; the
-// 16 extra bits make the final RNE step see every tie correctly).
-__device__ __forceinline__ uint32_t f64_to_bf16(double y) {
-  const float t = __double2float_rz(y);
+// Two floats -> packed bfloat16 pair (low half = a), round to nearest even,
+// with gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
+}
+
+// float64 -> float32 that rounds to the same bfloat16 as the float64 value
+// would directly (nearest, ties to even).  Rounding to float32 first is exact
+// for this purpose unless the float32 result lands exactly on a bfloat16 tie;
+// then it is moved one float32 step toward the float64 value (or kept when
+// the float64 value is the tie itself).
+__device__ __forceinline__ float f64_for_bf16(double y) {
+  const float t = (float)y;
   uint32_t u = __float_as_uint(t);
-  if ((double)t != y) u |= 1u;
-  return f2bf(__uint_as_float(u));
+  if ((u & 0xffffu) == 0x8000u) {
+    const double back = (double)t;
+    if (back != y) u = fabs(y) > fabs(back) ? u + 1u : u - 1u;
+  }
+  return __uint_as_float(u);
+}
+
+// float64 pair -> packed, correctly rounded bfloat16 pair.
+__device__ __forceinline__ uint32_t cvt2_bf16_f64(double a, double b) {
+  return cvt2_bf16(f64_for_bf16(a), f64_for_bf16(b));
+}
+
+// float64 -> bfloat16 bit pattern, correctly rounded (single value).
+__device__ __forceinline__ uint32_t f64_to_bf16(double y) {
+  return f2bf(f64_for_bf16(y));
 }
 
 // Rotation of one pair in float64: y1 = x1 c - x2 s, y2 = x1 s + x2 c.
