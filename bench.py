@@ -306,7 +306,20 @@ def main():
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch device-to-device copies of MIB MiB (10 launches): "
+                         "the known-size kernel that scales the HBM byte counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * 2 ** 20
+        x = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(10):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 10}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: streams are independent, so N GPUs would each "
               "run the same per-GPU workload on their own streams with no communication; "

@@ -79,6 +79,7 @@ struct VChunk<4> {
 };
 
 constexpr float kLazyMax = 8.0f;  // rescale only when the max grows by > 2^8
+constexpr bool INLOOP = false;    // fused updates on the tiles in registers (else a pre-pass)
 
 // Waves per SIMD the register allocation targets: the largest count that
 // fits without spilling (the compensated re-base keeps two more K arrays live).
@@ -104,7 +105,8 @@ void attn_kernel(AttnArgs a) {
   __shared__ float sm_o[NW > 1 ? NW - 1 : 1][8][D];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index made provably uniform, so tile-index branches are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15;
   const int g4 = lane >> 4;
   const int col_q = c & 7;       // query vector of this column
@@ -140,6 +142,32 @@ void attn_kernel(AttnArgs a) {
     if (KIND == kEncoderFused) return vec_off(j);
     return (((int64_t)l * a.S + s) * a.Hkv + g) * D;
   };
+
+  struct Tile {
+    u32x4 k[KS];
+    VT v[4];
+  };
+  // Rows past `lim` (the last row that may be read) are clamped to it, so a
+  // partial tile reads valid data; its masked keys get probability 0.
+  auto load_tile = [&](int key0, Tile& T, int lim) {
+    const int rk = key0 + c < lim ? key0 + c : lim;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) T.k[st] = ld16(Kp + rk * rs + 32 * st + 8 * g4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rv0 = key0 + 4 * g4 + j;
+      const int rv = rv0 < lim ? rv0 : lim;
+      T.v[j] = VC::load(Vp + rv * rs + CW * c);
+    }
+  };
+
+  // The wave's first tile is requested before the plan and the query are
+  // read (rows clamped into the allocation; rows past the valid range are
+  // masked in process()), so its latency overlaps the set-up below.
+  const int first = kb + TK * wave;
+  const int kalloc = kb + per < slots ? kb + per : slots;
+  Tile t0, t1;
+  load_tile(first, t0, kalloc - 1 > 0 ? kalloc - 1 : 0);
 
   // ---- rotated query, split into hi/lo bfloat16 columns, built once ----
   {
@@ -195,7 +223,7 @@ void attn_kernel(AttnArgs a) {
   // the stored row); lo: stored residual (compensated re-base); sgn = -1
   // rotates by the negative angle.
   auto rotate_row = [&](const u32x4* src, const u32x4* lo, const double* cs, const double* sn,
-                        double sgn, int row) {
+                        double sgn, int row, u32x4* kout) {
 #pragma unroll
     for (int st = 0; st < KH; ++st) {
       u32x4 w1, w2, r1, r2;
@@ -224,6 +252,10 @@ void attn_kernel(AttnArgs a) {
       }
       st16(Kp + row * rs + 32 * st + 8 * g4, w1);
       st16(Kp + row * rs + 32 * (st + KH) + 8 * g4, w2);
+      if (kout) {
+        kout[st] = w1;
+        kout[st + KH] = w2;
+      }
       if (COMP) {
         st16(Lp + row * rs + 32 * st + 8 * g4, r1);
         st16(Lp + row * rs + 32 * (st + KH) + 8 * g4, r2);
@@ -232,7 +264,7 @@ void attn_kernel(AttnArgs a) {
   };
 
   // ---- fused cache updates: a pre-pass over this wave's own tiles ----
-  if (KIND != kDecodeRead) {
+  if (KIND != kDecodeRead && !INLOOP) {
     for (int tt = wave;; tt += NW) {
       const int key0 = kb + TK * tt;
       if (key0 >= ke) break;
@@ -247,7 +279,7 @@ void attn_kernel(AttnArgs a) {
           const uint16_t* kn = a.knew + new_off(jn);
 #pragma unroll
           for (int st = 0; st < KS; ++st) src[st] = ld16(kn + 32 * st + 8 * g4);
-          rotate_row(src, nullptr, P->rope_new[jn][0], P->rope_new[jn][1], 1.0, row);
+          rotate_row(src, nullptr, P->rope_new[jn][0], P->rope_new[jn][1], 1.0, row, nullptr);
         } else if (delta != 0) {
           u32x4 src[KS], lo[KS];
 #pragma unroll
@@ -255,7 +287,7 @@ void attn_kernel(AttnArgs a) {
             src[st] = ld16(Kp + row * rs + 32 * st + 8 * g4);
             lo[st] = COMP ? ld16(Lp + row * rs + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
           }
-          rotate_row(src, COMP ? lo : nullptr, P->rope_delta[0], P->rope_delta[1], -1.0, row);
+          rotate_row(src, COMP ? lo : nullptr, P->rope_delta[0], P->rope_delta[1], -1.0, row, nullptr);
         }
       }
 #pragma unroll
@@ -285,45 +317,58 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < CW; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  struct Tile {
-    u32x4 k[KS];
-    VT v[4];
-  };
-  // rows clamped into the allocation (masked rows are never used)
-  auto load_tile = [&](int key0, Tile& T) {
-    const int rk = key0 + c < slots ? key0 + c : slots - 1;
-#pragma unroll
-    for (int st = 0; st < KS; ++st) T.k[st] = ld16(Kp + rk * rs + 32 * st + 8 * g4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rv0 = key0 + 4 * g4 + j;
-      const int rv = rv0 < slots ? rv0 : slots - 1;
-      T.v[j] = VC::load(Vp + rv * rs + CW * c);
-    }
-  };
-
   auto process = [&](Tile& T, int key0) {
+    if (KIND != kDecodeRead && INLOOP) {
+      // fused updates on the tile already in registers
+      const int row = key0 + c;
+      if (row < ke) {
+        const int jn = new_index(row);
+        if (jn >= 0) {
+          u32x4 src[KS];
+          const uint16_t* kn = a.knew + new_off(jn);
+#pragma unroll
+          for (int st = 0; st < KS; ++st) src[st] = ld16(kn + 32 * st + 8 * g4);
+          rotate_row(src, nullptr, P->rope_new[jn][0], P->rope_new[jn][1], 1.0, row, T.k);
+        } else if (delta != 0) {
+          u32x4 src[KS], lo[KS];
+#pragma unroll
+          for (int st = 0; st < KS; ++st) {
+            src[st] = T.k[st];
+            lo[st] = COMP ? ld16(Lp + row * rs + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
+          }
+          rotate_row(src, COMP ? lo : nullptr, P->rope_delta[0], P->rope_delta[1], -1.0, row,
+                     T.k);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rv = key0 + 4 * g4 + j;
+        if (rv >= ke) continue;
+        const int jn = new_index(rv);
+        if (jn >= 0) {
+          T.v[j] = VC::load(a.vnew + new_off(jn) + CW * c);
+          VC::store(Vp + rv * rs + CW * c, T.v[j]);
+        }
+      }
+    }
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < KS; ++st)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[st]), qop[st],
                                                     acc, 0, 0, 0);
-    const bool full = (KIND != kEncoderFused) && key0 + TK <= ke;
     float sv[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x = (acc[r] + dpp_ror8(acc[r])) * a.scale_log2;
-      if (!full) {
-        const int row = key0 + 4 * g4 + r;
-        bool vis = row < ke;
-        if (KIND == kEncoderFused) {
-          const int back = (slot_last - row + cap) % cap;
-          const int64_t kpos = last_pos - back;
-          vis = vis && kpos >= first_pos && kpos <= qpos;
-        }
-        x = vis ? x : -INFINITY;
+      const int row = key0 + 4 * g4 + r;
+      bool vis = row < ke;
+      if (KIND == kEncoderFused) {
+        const int back = (slot_last - row + cap) % cap;
+        const int64_t kpos = last_pos - back;
+        vis = vis && kpos >= first_pos && kpos <= qpos;
       }
+      x = vis ? x : -INFINITY;
       sv[r] = x;
       mx = fmaxf(mx, x);
     }
@@ -338,24 +383,21 @@ void attn_kernel(AttnArgs a) {
       for (int e = 0; e < CW; ++e) oacc[e] *= alpha;
     }
     float pj[4];
-    if (full) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pj[r] = fast_exp2(sv[r] - m_run);
-    } else {
+    for (int r = 0; r < 4; ++r) pj[r] = m_run == -INFINITY ? 0.f : fast_exp2(sv[r] - m_run);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pj[r] = m_run == -INFINITY ? 0.f : fast_exp2(sv[r] - m_run);
+    for (int j = 0; j < 4; ++j) {
+      const bool live = key0 + 4 * g4 + j < ke;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (key0 + 4 * g4 + j >= ke) T.v[j] = VC::zero();
+      for (int w = 0; w < CW / 2; ++w) T.v[j][w] = live ? T.v[j][w] : 0u;
     }
     l_run += (pj[0] + pj[1]) + (pj[2] + pj[3]);
     const uint32_t h01 = cvt2_bf16(pj[0], pj[1]);
     const uint32_t h23 = cvt2_bf16(pj[2], pj[3]);
-    uint32_t p01 = h01, p23 = h23;
-    if (part) {
-      p01 = cvt2_bf16(pj[0] - bf2f(h01 & 0xffffu), pj[1] - bf2f(h01 >> 16));
-      p23 = cvt2_bf16(pj[2] - bf2f(h23 & 0xffffu), pj[3] - bf2f(h23 >> 16));
-    }
+    const uint32_t l01 = cvt2_bf16(pj[0] - bf2f(h01 & 0xffffu), pj[1] - bf2f(h01 >> 16));
+    const uint32_t l23 = cvt2_bf16(pj[2] - bf2f(h23 & 0xffffu), pj[3] - bf2f(h23 >> 16));
+    const uint32_t p01 = part ? l01 : h01;
+    const uint32_t p23 = part ? l23 : h23;
     const s16x4 pop = __builtin_bit_cast(s16x4, u32x2{p01, p23});
 
     // V^T operand: dims CW*c + e of the tile's 4 keys of this lane group
@@ -369,23 +411,33 @@ void attn_kernel(AttnArgs a) {
     }
   };
 
-  // ---- main loop: two tiles in registers, the next one loading ----
-  Tile t0, t1;
-  int tile = wave;
-  if (kb + TK * tile < ke) load_tile(kb + TK * tile, t0);
-  for (;;) {
-    const int key0 = kb + TK * tile;
-    if (key0 >= ke) break;
-    int nxt = tile + NW;
-    if (kb + TK * nxt < ke) load_tile(kb + TK * nxt, t1);
-    process(t0, key0);
-    tile = nxt;
-    const int key1 = kb + TK * tile;
-    if (key1 >= ke) break;
-    nxt = tile + NW;
-    if (kb + TK * nxt < ke) load_tile(kb + TK * nxt, t0);
-    process(t1, key1);
-    tile = nxt;
+  // ---- main loop: one tile loading while the previous one computes ----
+  // The trip count is uniform and the prefetch unconditional inside the loop,
+  // so the compiler can keep the next tile's loads in flight across the
+  // current tile's math (a conditional prefetch makes it wait for everything).
+  const int ntiles = first < ke ? (ke - first + TK * NW - 1) / (TK * NW) : 0;
+  const int lim = ke - 1;
+  auto key_of = [&](int i) { return first + TK * NW * i; };
+  if (KIND != kDecodeRead) {
+    const bool rewritten = delta != 0 || KIND == kEncoderFused ||
+                           (slot_new >= first && slot_new < first + TK);
+    if (rewritten && ntiles > 0) load_tile(first, t0, lim);
+  }
+  if (ntiles > 0) {
+    int i = 0;
+    for (; i + 2 < ntiles; i += 2) {
+      load_tile(key_of(i + 1), t1, lim);
+      process(t0, key_of(i));
+      load_tile(key_of(i + 2), t0, lim);
+      process(t1, key_of(i + 1));
+    }
+    if (ntiles - i == 2) {
+      load_tile(key_of(i + 1), t1, lim);
+      process(t0, key_of(i));
+      process(t1, key_of(i + 1));
+    } else {
+      process(t0, key_of(i));
+    }
   }
 
   // ---- per-wave reduction: row sums over lane groups, hi+lo columns ----

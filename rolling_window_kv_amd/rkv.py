@@ -265,18 +265,34 @@ def rkv_encoder_chunk_attn(cfg, plan, kv, q, k_new, v_new, out, workspace=None, 
 # ---------------------------------------------------------------------------
 
 class Cache:
-    """Device tensors of one rolling cache: rings, per-stream state, plan, workspace."""
+    """Device tensors of one rolling cache: rings, per-stream state, plan, workspace.
 
-    def __init__(self, cfg, slots, window, cap, origin=0, device="cuda", zero=True):
+    layout "interleaved" (default): one buffer [L, S, Hkv, slots, n, d] with K,
+    V (and the compensated residual) of a slot side by side, so a slot's rows
+    are one contiguous stream; "separate": three [L, S, Hkv, slots, d] tensors.
+    Either is described to the library through strides (rkv_kv_view).
+    """
+
+    def __init__(self, cfg, slots, window, cap, origin=0, device="cuda", zero=True,
+                 layout="interleaved"):
         import torch
         self.cfg = cfg
         L, S, H, d = cfg.num_layers, cfg.num_streams, cfg.num_kv_heads, cfg.head_dim
-        shape = (L, S, H, slots, d)
+        comp = bool(cfg.flags & RKV_F_COMPENSATED)
         alloc = torch.zeros if zero else torch.empty
-        self.k = alloc(shape, dtype=torch.bfloat16, device=device)
-        self.v = alloc(shape, dtype=torch.bfloat16, device=device)
-        self.k_lo = (alloc(shape, dtype=torch.bfloat16, device=device)
-                     if cfg.flags & RKV_F_COMPENSATED else None)
+        if layout == "interleaved":
+            n = 3 if comp else 2
+            self.buf = alloc((L, S, H, slots, n, d), dtype=torch.bfloat16, device=device)
+            self.k = self.buf[:, :, :, :, 0, :]
+            self.v = self.buf[:, :, :, :, 1, :]
+            self.k_lo = self.buf[:, :, :, :, 2, :] if comp else None
+        elif layout == "separate":
+            shape = (L, S, H, slots, d)
+            self.k = alloc(shape, dtype=torch.bfloat16, device=device)
+            self.v = alloc(shape, dtype=torch.bfloat16, device=device)
+            self.k_lo = alloc(shape, dtype=torch.bfloat16, device=device) if comp else None
+        else:
+            raise ValueError(layout)
         self.kv = kv_view(self.k, self.v, self.k_lo)
         host = rkv_state_init_host(cfg, window, cap, origin)
         self.state = torch.from_numpy(host.view(np.uint8).copy()).to(device)
