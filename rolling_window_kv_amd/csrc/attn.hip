@@ -100,6 +100,8 @@ void attn_kernel(AttnArgs a) {
   typedef typename VC::T VT;
 
   __shared__ u32x4 sm_q[KS][64];
+  __shared__ u32x4 sm_newk[KS][4];   // decoder: the appended K row, chunk (st, g4)
+  __shared__ VT sm_newv[16];         // decoder: the appended V row, chunk c
   __shared__ float sm_m[NW][8];
   __shared__ float sm_l[NW][8];
   __shared__ float sm_o[NW > 1 ? NW - 1 : 1][8][D];
@@ -166,8 +168,18 @@ void attn_kernel(AttnArgs a) {
   // masked in process()), so its latency overlaps the set-up below.
   const int first = kb + TK * wave;
   const int kalloc = kb + per < slots ? kb + per : slots;
-  Tile t0, t1;
-  load_tile(first, t0, kalloc - 1 > 0 ? kalloc - 1 : 0);
+  Tile tb[2];
+  load_tile(first, tb[0], kalloc - 1 > 0 ? kalloc - 1 : 0);
+  // The decoder's new K/V row is requested now too; it is patched into its
+  // tile inside the attention loop (RoPE-on-append without a serial pre-step).
+  u32x4 knew_c[KS];
+  VT vnew_c;
+  if (KIND == kDecodeFused) {
+    const uint16_t* kn = a.knew + new_off(0);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) knew_c[st] = ld16(kn + 32 * st + 8 * g4);
+    vnew_c = VC::load(a.vnew + new_off(0) + CW * c);
+  }
 
   // ---- rotated query, split into hi/lo bfloat16 columns, built once ----
   {
@@ -264,13 +276,91 @@ void attn_kernel(AttnArgs a) {
   };
 
   // ---- fused cache updates: a pre-pass over this wave's own tiles ----
+  auto key_of = [&](int i) { return first + TK * NW * i; };
+  const int ntiles = first < ke ? (ke - first + TK * NW - 1) / (TK * NW) : 0;
   if (KIND != kDecodeRead && !INLOOP) {
-    for (int tt = wave;; tt += NW) {
-      const int key0 = kb + TK * tt;
-      if (key0 >= ke) break;
+    // (1) Exact re-base of every retained row of the wave's tiles when the
+    // base moved (delta != 0).  The lane's cos/sin(delta theta_i) stay in
+    // registers and the next tile's rows load while the current one rotates.
+    if (KIND == kDecodeFused && delta != 0) {
+      // one pass per chunk pair (st, st + KH): 8 rotary pairs' tables live
+      for (int st = 0; st < KH; ++st) {
+        double dcs[8], dsn[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 32 * st + 8 * g4 + e;
+          dcs[e] = P->rope_delta[0][i];
+          dsn[e] = -P->rope_delta[1][i];
+        }
+        const int o1 = 32 * st + 8 * g4, o2 = 32 * (st + KH) + 8 * g4;
+        auto ldrow = [&](int i, u32x4* k) {
+          const int row = key_of(i) + c < ke ? key_of(i) + c : ke - 1;
+          k[0] = ld16(Kp + row * rs + o1);
+          k[1] = ld16(Kp + row * rs + o2);
+          if (COMP) {
+            k[2] = ld16(Lp + row * rs + o1);
+            k[3] = ld16(Lp + row * rs + o2);
+          }
+        };
+        auto rebase_row = [&](int i, const u32x4* k) {
+          const int row = key_of(i) + c;
+          if (row >= ke || new_index(row) >= 0) return;
+          u32x4 w1, w2, r1, r2;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            double y1[2], y2[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int e = 2 * w + h;
+              double x1 = bf2f(elem8(k[0], e)), x2 = bf2f(elem8(k[1], e));
+              if (COMP) {
+                x1 += (double)bf2f(elem8(k[2], e));
+                x2 += (double)bf2f(elem8(k[3], e));
+              }
+              rotate_pair64(x1, x2, dcs[e], dsn[e], y1[h], y2[h]);
+            }
+            w1[w] = cvt2_bf16_f64(y1[0], y1[1]);
+            w2[w] = cvt2_bf16_f64(y2[0], y2[1]);
+            if (COMP) {
+              r1[w] = cvt2_bf16_f64(y1[0] - (double)bf2f(w1[w] & 0xffffu),
+                                    y1[1] - (double)bf2f(w1[w] >> 16));
+              r2[w] = cvt2_bf16_f64(y2[0] - (double)bf2f(w2[w] & 0xffffu),
+                                    y2[1] - (double)bf2f(w2[w] >> 16));
+            }
+          }
+          st16(Kp + row * rs + o1, w1);
+          st16(Kp + row * rs + o2, w2);
+          if (COMP) {
+            st16(Lp + row * rs + o1, r1);
+            st16(Lp + row * rs + o2, r2);
+          }
+        };
+        if (ntiles > 0) {
+          u32x4 ka[4], kb2[4];
+          ldrow(0, ka);
+          int i = 0;
+          for (; i + 2 < ntiles; i += 2) {
+            ldrow(i + 1, kb2);
+            rebase_row(i, ka);
+            ldrow(i + 2, ka);
+            rebase_row(i + 1, kb2);
+          }
+          if (ntiles - i == 2) {
+            ldrow(i + 1, kb2);
+            rebase_row(i, ka);
+            rebase_row(i + 1, kb2);
+          } else {
+            rebase_row(i, ka);
+          }
+        }
+      }
+    }
+    // (2) Encoder: RoPE-on-append of the new frames that fall in the wave's tiles.
+    for (int tt = 0; KIND == kEncoderFused && tt < ntiles; ++tt) {
+      const int key0 = key_of(tt);
       bool any_new = true;
       if (KIND == kDecodeFused) any_new = slot_new >= key0 && slot_new < key0 + TK;
-      if (delta == 0 && !any_new) continue;
+      if (!any_new) continue;
       const int row = key0 + c;
       if (row < ke) {
         const int jn = new_index(row);
@@ -280,14 +370,6 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int st = 0; st < KS; ++st) src[st] = ld16(kn + 32 * st + 8 * g4);
           rotate_row(src, nullptr, P->rope_new[jn][0], P->rope_new[jn][1], 1.0, row, nullptr);
-        } else if (delta != 0) {
-          u32x4 src[KS], lo[KS];
-#pragma unroll
-          for (int st = 0; st < KS; ++st) {
-            src[st] = ld16(Kp + row * rs + 32 * st + 8 * g4);
-            lo[st] = COMP ? ld16(Lp + row * rs + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
-          }
-          rotate_row(src, COMP ? lo : nullptr, P->rope_delta[0], P->rope_delta[1], -1.0, row, nullptr);
         }
       }
 #pragma unroll
@@ -300,7 +382,50 @@ void attn_kernel(AttnArgs a) {
     }
   }
 
-  __syncthreads();  // the query operand is in LDS
+  // Decoder RoPE-on-append: wave 0 rotates the new K row (float64, correctly
+  // rounded), writes K and V to the ring and leaves both in LDS for the wave
+  // whose tile holds the new slot.
+  if (KIND == kDecodeFused && !INLOOP && wave == 0) {
+#pragma unroll
+    for (int st = 0; st < KH; ++st) {
+      u32x4 w1, w2, r1, r2;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        double y1[2], y2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = 2 * w + h;
+          const int i = 32 * st + 8 * g4 + e;
+          rotate_pair64(bf2f(elem8(knew_c[st], e)), bf2f(elem8(knew_c[st + KH], e)),
+                        P->rope_new[0][0][i], P->rope_new[0][1][i], y1[h], y2[h]);
+        }
+        w1[w] = cvt2_bf16_f64(y1[0], y1[1]);
+        w2[w] = cvt2_bf16_f64(y2[0], y2[1]);
+        if (COMP) {
+          r1[w] = cvt2_bf16_f64(y1[0] - (double)bf2f(w1[w] & 0xffffu),
+                                y1[1] - (double)bf2f(w1[w] >> 16));
+          r2[w] = cvt2_bf16_f64(y2[0] - (double)bf2f(w2[w] & 0xffffu),
+                                y2[1] - (double)bf2f(w2[w] >> 16));
+        }
+      }
+      if (c == 0) {
+        sm_newk[st][g4] = w1;
+        sm_newk[st + KH][g4] = w2;
+        st16(Kp + slot_new * rs + 32 * st + 8 * g4, w1);
+        st16(Kp + slot_new * rs + 32 * (st + KH) + 8 * g4, w2);
+        if (COMP) {
+          st16(Lp + slot_new * rs + 32 * st + 8 * g4, r1);
+          st16(Lp + slot_new * rs + 32 * (st + KH) + 8 * g4, r2);
+        }
+      }
+    }
+    if (g4 == 0) {
+      sm_newv[c] = vnew_c;
+      VC::store(Vp + slot_new * rs + CW * c, vnew_c);
+    }
+  }
+
+  __syncthreads();  // the query operand (and the decoder's new row) is in LDS
   bf16x8 qop[KS];
 #pragma unroll
   for (int st = 0; st < KS; ++st) qop[st] = __builtin_bit_cast(bf16x8, sm_q[st][lane]);
@@ -318,6 +443,19 @@ void attn_kernel(AttnArgs a) {
   for (int e = 0; e < CW; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto process = [&](Tile& T, int key0) {
+    if (KIND == kDecodeFused && !INLOOP && slot_new >= key0 && slot_new < key0 + TK) {
+      // the new row lies in this tile: take its rotated K and V from LDS
+      const int r = slot_new - key0;
+      if (c == r) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) T.k[st] = sm_newk[st][g4];
+      }
+      if (g4 == (r >> 2)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j == (r & 3)) T.v[j] = sm_newv[c];
+      }
+    }
     if (KIND != kDecodeRead && INLOOP) {
       // fused updates on the tile already in registers
       const int row = key0 + c;
@@ -415,15 +553,18 @@ void attn_kernel(AttnArgs a) {
   // The trip count is uniform and the prefetch unconditional inside the loop,
   // so the compiler can keep the next tile's loads in flight across the
   // current tile's math (a conditional prefetch makes it wait for everything).
-  const int ntiles = first < ke ? (ke - first + TK * NW - 1) / (TK * NW) : 0;
   const int lim = ke - 1;
-  auto key_of = [&](int i) { return first + TK * NW * i; };
   if (KIND != kDecodeRead) {
-    const bool rewritten = delta != 0 || KIND == kEncoderFused ||
-                           (slot_new >= first && slot_new < first + TK);
-    if (rewritten && ntiles > 0) load_tile(first, t0, lim);
+    const bool rewritten = delta != 0 || KIND == kEncoderFused;
+    if (rewritten && ntiles > 0) load_tile(first, tb[0], lim);
   }
+  // One tile loads while the previous one computes.  The trip count is
+  // uniform and the prefetch unconditional inside the loop, so the compiler
+  // keeps the next tile's loads in flight across the current tile's math (a
+  // conditional prefetch makes it wait for every outstanding load).
   if (ntiles > 0) {
+    Tile& t0 = tb[0];
+    Tile& t1 = tb[1];
     int i = 0;
     for (; i + 2 < ntiles; i += 2) {
       load_tile(key_of(i + 1), t1, lim);
