@@ -263,9 +263,24 @@ def run_gpu(c, args):
         if ev is not None:
             ev[1].record(stream)
 
+    def fill(i):
+        # Untimed set-up: the same cache updates as a step, without attention
+        # (identical ring contents), so every launch of the attention kernel
+        # in the run is a full-window one.
+        j = i % P
+        rkv.rkv_advance(cfg, cache.state, cache.plan, sp)
+        if c["mode"] == "compact":
+            rkv.rkv_compact(cfg, cache.plan, cache.kv, sp)
+        if c["mode"] == "rebase":
+            rkv.rkv_roll_rebase(cfg, cache.plan, cache.kv, sp)
+        rkv.rkv_append(cfg, cache.plan, cache.kv, k[j], v[j], sp)
+
     i = 0
     for _ in range(prefill):          # fill every window (untimed set-up)
-        step(i)
+        if c["mode"] == "enc":
+            step(i)
+        else:
+            fill(i)
         i += 1
     for _ in range(args.warmup):
         step(i)
@@ -294,6 +309,53 @@ def run_gpu(c, args):
                 setup_s=setup_s, prefill=prefill)
 
 
+def summarize_rocprof(root):
+    """Per-kernel figures from a rocprofv3 CSV output folder: its own --stats
+    table, mean dispatch duration from the kernel trace, and mean counter
+    values per dispatch (FETCH_SIZE / WRITE_SIZE are in KiB)."""
+    import csv
+    import glob
+    from collections import OrderedDict, defaultdict
+
+    def short(name):
+        return name if len(name) <= 110 else name[:107] + "..."
+
+    lines = []
+    for path in sorted(glob.glob(os.path.join(root, "**", "*_kernel_stats.csv"), recursive=True)):
+        lines.append(f"# rocprofv3 --stats: {os.path.relpath(path, root)}")
+        lines.append(f"{'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel")
+        for r in csv.DictReader(open(path)):
+            lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
+                         f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                         f"{float(r['Percentage']):6.2f}  {short(r['Name'])}")
+    for path in sorted(glob.glob(os.path.join(root, "**", "*_kernel_trace.csv"), recursive=True)):
+        dur = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            dur[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        lines.append(f"# kernel trace: {os.path.relpath(path, root)}")
+        lines.append(f"{'calls':>7} {'mean_us':>10} {'median_us':>10}  kernel")
+        for name, d in sorted(dur.items(), key=lambda x: -sum(x[1])):
+            lines.append(f"{len(d):7d} {np.mean(d) / 1e3:10.2f} {np.median(d) / 1e3:10.2f}  "
+                         f"{short(name)}")
+    for path in sorted(glob.glob(os.path.join(root, "**", "*_counter_collection.csv"),
+                            recursive=True)):
+        per = OrderedDict()
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            per.setdefault(key, defaultdict(float))[r["Counter_Name"]] += float(r["Counter_Value"])
+        agg = defaultdict(lambda: defaultdict(list))
+        for (name, _), cnt in per.items():
+            for cn, v in cnt.items():
+                agg[name][cn].append(v)
+        lines.append(f"# counters per dispatch: {os.path.relpath(path, root)}")
+        lines.append(f"{'dispatches':>10} {'counter':>12} {'mean':>16} {'min':>16} {'max':>16}  kernel")
+        for name, cs in agg.items():
+            for cn, v in cs.items():
+                lines.append(f"{len(v):10d} {cn:>12} {np.mean(v):16.1f} {np.min(v):16.1f} "
+                             f"{np.max(v):16.1f}  {short(name)}")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,7 +371,12 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch device-to-device copies of MIB MiB (10 launches): "
                          "the known-size kernel that scales the HBM byte counters")
+    ap.add_argument("--summarize-rocprof", metavar="DIR", default=None,
+                    help="print per-kernel figures from a rocprofv3 CSV output folder and exit")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        print(summarize_rocprof(args.summarize_rocprof))
+        return
     if args.copy_calibration:
         import torch
         n = args.copy_calibration * 2 ** 20

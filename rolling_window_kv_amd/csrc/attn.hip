@@ -2,10 +2,13 @@
 //
 // One workgroup of NW waves handles one (layer, stream, kv head) item -- or
 // one split of its key range.  The waves take 16-key tiles in turn, each
-// loading its next tile while it computes the current one, and merge their
-// partial softmax states through LDS at the end.  The G query vectors that
-// share the KV head (the 8 query heads of a GQA group, or the F frames of an
-// encoder chunk) form the N side of the matrix-core products:
+// keeping two tiles in registers (one computing, one loading), and merge their
+// partial softmax states through LDS at the end.  With the whole chip
+// streaming, a workgroup's life is set by its share of its CU's bandwidth, so
+// more waves per item (shorter lives) mainly shortens the drain at the end of
+// the launch, when too few workgroups remain to keep HBM busy.  The G query
+// vectors that share the KV head (the 8 query heads of a GQA group, or the F
+// frames of an encoder chunk) form the N side of the matrix-core products:
 //
 //   scores  S[key][col] = K[key][:] . Qt[:][col]   v_mfma_f32_16x16x32_bf16
 //   output  O[d][col]  += Vt[d][key] . P[key][col]  v_mfma_f32_16x16x16_bf16
@@ -27,17 +30,23 @@
 // lane (g4, c < 8) ends with dims [4*CW*g4, 4*CW*g4 + 4*CW) of column c.
 //
 // The rotated query is built once per workgroup (the waves split the rotary
-// pairs) and shared through LDS.  Softmax is online with a lazily moved
+// pairs) and shared through LDS.  Each wave requests its query chunks, rotary
+// tables and new row first and its first two tiles right after them (vector
+// loads complete in issue order), so set-up waits only for the small loads
+// and runs with two tiles in flight.  Softmax is online with a lazily moved
 // maximum: probabilities use the running maximum m until a tile's maximum
 // exceeds it by more than 2^8 (log2 units), so accumulator rescaling is rare.
 //
 // The fused kinds also update the cache in the same launch, with results
 // identical to running rkv_roll_rebase, rkv_append and the read-only kind in
-// turn: before its attention loop each wave rotates the new row(s) of its
-// tiles from k_new in float64 and writes them (RoPE-on-append), and in REBASE
-// mode, when the plan's delta D > 0, rotates every other retained row of its
-// tiles by R(-D) in float64 and writes it back (exact re-base).  The attention
-// loop then reads those rows back; each tile is owned by one wave.
+// turn.  Decoder: during set-up the waves rotate the new K row from k_new in
+// float64 (one rotary chunk pair each), write K and V to the ring and leave
+// both in LDS, from where the wave whose tile holds the new slot patches them
+// into its registers (its tile may have been read before the write).  In
+// REBASE mode, when the plan's delta D > 0, each wave first rotates every other
+// retained row of its own tiles by R(-D) in float64, writes it back (exact
+// re-base) and reads its first tiles again.  Encoder: each wave writes the new
+// frames that fall in its own tiles before reading them.
 
 #include "rkv_device.h"
 #include "rkv_internal.h"
@@ -104,7 +113,7 @@ void attn_kernel(AttnArgs a) {
   __shared__ VT sm_newv[16];         // decoder: the appended V row, chunk c
   __shared__ float sm_m[NW][8];
   __shared__ float sm_l[NW][8];
-  __shared__ float sm_o[NW > 1 ? NW - 1 : 1][8][D];
+  __shared__ f32x4 sm_o[NW > 1 ? NW - 1 : 1][CW][32];  // [wave-1][e][8*g4 + c], c < 8
 
   const int lane = threadIdx.x & 63;
   // wave index made provably uniform, so tile-index branches are scalar
@@ -163,34 +172,63 @@ void attn_kernel(AttnArgs a) {
     }
   };
 
-  // The wave's first tile is requested before the plan and the query are
-  // read (rows clamped into the allocation; rows past the valid range are
-  // masked in process()), so its latency overlaps the set-up below.
-  const int first = kb + TK * wave;
-  const int kalloc = kb + per < slots ? kb + per : slots;
-  Tile tb[2];
-  load_tile(first, tb[0], kalloc - 1 > 0 ? kalloc - 1 : 0);
-  // The decoder's new K/V row is requested now too; it is patched into its
-  // tile inside the attention loop (RoPE-on-append without a serial pre-step).
-  u32x4 knew_c[KS];
+  // ---- loads issued before any result is needed ----
+  // Order matters: vector loads complete in issue order, so the query and its
+  // rotary tables come first (the set-up waits only for them) and the wave's
+  // first two tiles after them, so that set-up runs with two tiles in flight.
+  // Tiles read here are clamped into the allocation (rows past the valid
+  // range are masked in process()).
+  //
+  // Rotated query: wave w builds the rotary chunk pair (st, st + KH) with
+  // st = w, split into hi/lo bfloat16 columns, and shares it through LDS.
+  constexpr int QST = (KH + NW - 1) / NW;  // chunk pairs per wave
+  const bool qhas = col_q < a.G;
+  u32x4 qx1[QST], qx2[QST];
+  // cos/sin of this lane's rotary pairs at the new position (float64: the
+  // decoder's new K row uses them as they are, the query in float32)
+  double rcs[QST][8], rsn[QST][8];
+  {
+    const uint16_t* qp = a.q + vec_off(qhas ? col_q : 0);
+    const int rrow = (KIND == kEncoderFused) ? col_q : 0;
+#pragma unroll
+    for (int k = 0; k < QST; ++k) {
+      const int st = wave + NW * k < KH ? wave + NW * k : KH - 1;
+      qx1[k] = qhas ? ld16(qp + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
+      qx2[k] = qhas ? ld16(qp + 32 * (st + KH) + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        rcs[k][e] = P->rope_new[rrow][0][32 * st + 8 * g4 + e];
+        rsn[k][e] = P->rope_new[rrow][1][32 * st + 8 * g4 + e];
+      }
+    }
+  }
+  // Decoder's new row: wave w rotates K chunk pair (st = w, st + KH); the last
+  // wave copies V.  Both are patched into their tile from LDS inside the loop.
+  u32x4 knew_c[QST][2];
   VT vnew_c;
   if (KIND == kDecodeFused) {
     const uint16_t* kn = a.knew + new_off(0);
 #pragma unroll
-    for (int st = 0; st < KS; ++st) knew_c[st] = ld16(kn + 32 * st + 8 * g4);
+    for (int k = 0; k < QST; ++k) {
+      const int st = wave + NW * k < KH ? wave + NW * k : KH - 1;
+      knew_c[k][0] = ld16(kn + 32 * st + 8 * g4);
+      knew_c[k][1] = ld16(kn + 32 * (st + KH) + 8 * g4);
+    }
     vnew_c = VC::load(a.vnew + new_off(0) + CW * c);
   }
+  // keep the tile loads behind the set-up loads in issue order
+  __builtin_amdgcn_sched_barrier(0);
+  const int first = kb + TK * wave;
+  const int kalloc = kb + per < slots ? kb + per : slots;
+  Tile tb[2];
+  load_tile(first, tb[0], kalloc - 1 > 0 ? kalloc - 1 : 0);
+  load_tile(first + TK * NW, tb[1], kalloc - 1 > 0 ? kalloc - 1 : 0);
 
-  // ---- rotated query, split into hi/lo bfloat16 columns, built once ----
   {
-    const bool has = col_q < a.G;
-    const uint16_t* qp = a.q + vec_off(has ? col_q : 0);
-    const int rrow = (KIND == kEncoderFused) ? col_q : 0;
-    for (int st = wave; st < KH; st += NW) {
-      const u32x4 x1 = has ? ld16(qp + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 x2 = has ? ld16(qp + 32 * (st + KH) + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
-      const double* cs = P->rope_new[rrow][0] + 32 * st + 8 * g4;
-      const double* sn = P->rope_new[rrow][1] + 32 * st + 8 * g4;
+#pragma unroll
+    for (int k = 0; k < QST; ++k) {
+      const int st = wave + NW * k;
+      if (st >= KH) continue;
       u32x4 w1, w2;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -198,8 +236,8 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int e = 2 * w + h;
-          const float a1 = bf2f(elem8(x1, e)), a2 = bf2f(elem8(x2, e));
-          const float cq = (float)cs[e], sq = (float)sn[e];
+          const float a1 = bf2f(elem8(qx1[k], e)), a2 = bf2f(elem8(qx2[k], e));
+          const float cq = (float)rcs[k][e], sq = (float)rsn[k][e];
           y1[h] = fmaf(a1, cq, -(a2 * sq));
           y2[h] = fmaf(a1, sq, a2 * cq);
         }
@@ -275,9 +313,55 @@ void attn_kernel(AttnArgs a) {
     }
   };
 
+  // Decoder RoPE-on-append: the waves rotate the new K row (float64,
+  // correctly rounded) chunk pair by chunk pair, write K and V to the ring and
+  // leave both in LDS for the wave whose tile holds the new slot.
+  if (KIND == kDecodeFused && !INLOOP) {
+#pragma unroll
+    for (int k = 0; k < QST; ++k) {
+      const int st = wave + NW * k;
+      if (st >= KH) continue;
+      u32x4 w1, w2, r1, r2;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        double y1[2], y2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = 2 * w + h;
+          const int i = 32 * st + 8 * g4 + e;
+          rotate_pair64(bf2f(elem8(knew_c[k][0], e)), bf2f(elem8(knew_c[k][1], e)), rcs[k][e],
+                        rsn[k][e], y1[h], y2[h]);
+        }
+        w1[w] = cvt2_bf16_f64(y1[0], y1[1]);
+        w2[w] = cvt2_bf16_f64(y2[0], y2[1]);
+        if (COMP) {
+          r1[w] = cvt2_bf16_f64(y1[0] - (double)bf2f(w1[w] & 0xffffu),
+                                y1[1] - (double)bf2f(w1[w] >> 16));
+          r2[w] = cvt2_bf16_f64(y2[0] - (double)bf2f(w2[w] & 0xffffu),
+                                y2[1] - (double)bf2f(w2[w] >> 16));
+        }
+      }
+      if (c == 0) {
+        sm_newk[st][g4] = w1;
+        sm_newk[st + KH][g4] = w2;
+        st16(Kp + slot_new * rs + 32 * st + 8 * g4, w1);
+        st16(Kp + slot_new * rs + 32 * (st + KH) + 8 * g4, w2);
+        if (COMP) {
+          st16(Lp + slot_new * rs + 32 * st + 8 * g4, r1);
+          st16(Lp + slot_new * rs + 32 * (st + KH) + 8 * g4, r2);
+        }
+      }
+    }
+    if (wave == NW - 1 && g4 == 0) {
+      sm_newv[c] = vnew_c;
+      VC::store(Vp + slot_new * rs + CW * c, vnew_c);
+    }
+  }
+
   // ---- fused cache updates: a pre-pass over this wave's own tiles ----
   auto key_of = [&](int i) { return first + TK * NW * i; };
   const int ntiles = first < ke ? (ke - first + TK * NW - 1) / (TK * NW) : 0;
+  const int lim0 = ke > 0 ? ke - 1 : 0;  // last readable row of the valid range
   if (KIND != kDecodeRead && !INLOOP) {
     // (1) Exact re-base of every retained row of the wave's tiles when the
     // base moved (delta != 0).  The lane's cos/sin(delta theta_i) stay in
@@ -354,6 +438,9 @@ void attn_kernel(AttnArgs a) {
           }
         }
       }
+      // the early tiles are stale: read the re-based rows back
+      load_tile(first, tb[0], lim0);
+      load_tile(key_of(1), tb[1], lim0);
     }
     // (2) Encoder: RoPE-on-append of the new frames that fall in the wave's tiles.
     for (int tt = 0; KIND == kEncoderFused && tt < ntiles; ++tt) {
@@ -380,48 +467,10 @@ void attn_kernel(AttnArgs a) {
         if (jn >= 0) VC::store(Vp + rv * rs + CW * c, VC::load(a.vnew + new_off(jn) + CW * c));
       }
     }
-  }
-
-  // Decoder RoPE-on-append: wave 0 rotates the new K row (float64, correctly
-  // rounded), writes K and V to the ring and leaves both in LDS for the wave
-  // whose tile holds the new slot.
-  if (KIND == kDecodeFused && !INLOOP && wave == 0) {
-#pragma unroll
-    for (int st = 0; st < KH; ++st) {
-      u32x4 w1, w2, r1, r2;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        double y1[2], y2[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int e = 2 * w + h;
-          const int i = 32 * st + 8 * g4 + e;
-          rotate_pair64(bf2f(elem8(knew_c[st], e)), bf2f(elem8(knew_c[st + KH], e)),
-                        P->rope_new[0][0][i], P->rope_new[0][1][i], y1[h], y2[h]);
-        }
-        w1[w] = cvt2_bf16_f64(y1[0], y1[1]);
-        w2[w] = cvt2_bf16_f64(y2[0], y2[1]);
-        if (COMP) {
-          r1[w] = cvt2_bf16_f64(y1[0] - (double)bf2f(w1[w] & 0xffffu),
-                                y1[1] - (double)bf2f(w1[w] >> 16));
-          r2[w] = cvt2_bf16_f64(y2[0] - (double)bf2f(w2[w] & 0xffffu),
-                                y2[1] - (double)bf2f(w2[w] >> 16));
-        }
-      }
-      if (c == 0) {
-        sm_newk[st][g4] = w1;
-        sm_newk[st + KH][g4] = w2;
-        st16(Kp + slot_new * rs + 32 * st + 8 * g4, w1);
-        st16(Kp + slot_new * rs + 32 * (st + KH) + 8 * g4, w2);
-        if (COMP) {
-          st16(Lp + slot_new * rs + 32 * st + 8 * g4, r1);
-          st16(Lp + slot_new * rs + 32 * (st + KH) + 8 * g4, r2);
-        }
-      }
-    }
-    if (g4 == 0) {
-      sm_newv[c] = vnew_c;
-      VC::store(Vp + slot_new * rs + CW * c, vnew_c);
+    if (KIND == kEncoderFused) {
+      // the early tiles are stale: read the appended rows back
+      load_tile(first, tb[0], lim0);
+      load_tile(key_of(1), tb[1], lim0);
     }
   }
 
@@ -549,35 +598,39 @@ void attn_kernel(AttnArgs a) {
     }
   };
 
-  // ---- main loop: one tile loading while the previous one computes ----
-  // The trip count is uniform and the prefetch unconditional inside the loop,
-  // so the compiler can keep the next tile's loads in flight across the
-  // current tile's math (a conditional prefetch makes it wait for everything).
-  const int lim = ke - 1;
-  if (KIND != kDecodeRead) {
-    const bool rewritten = delta != 0 || KIND == kEncoderFused;
-    if (rewritten && ntiles > 0) load_tile(first, tb[0], lim);
-  }
-  // One tile loads while the previous one computes.  The trip count is
-  // uniform and the prefetch unconditional inside the loop, so the compiler
-  // keeps the next tile's loads in flight across the current tile's math (a
-  // conditional prefetch makes it wait for every outstanding load).
+  // ---- main loop: two tiles in registers, the one just used reloading ----
+  // The trip count is uniform and the loads unconditional inside the loop, so
+  // the compiler keeps the next tile's loads in flight across the current
+  // tile's math (a conditional load makes it wait for every outstanding load).
+  const int lim = lim0;
   if (ntiles > 0) {
     Tile& t0 = tb[0];
     Tile& t1 = tb[1];
+    // tiles 0 and 1 are already in flight
     int i = 0;
-    for (; i + 2 < ntiles; i += 2) {
-      load_tile(key_of(i + 1), t1, lim);
-      process(t0, key_of(i));
-      load_tile(key_of(i + 2), t0, lim);
-      process(t1, key_of(i + 1));
-    }
-    if (ntiles - i == 2) {
-      load_tile(key_of(i + 1), t1, lim);
-      process(t0, key_of(i));
-      process(t1, key_of(i + 1));
+    if (ntiles > 2) {
+      process(t0, key_of(0));
+      load_tile(key_of(2), t0, lim);
+      process(t1, key_of(1));
+      i = 2;
+      for (; i + 2 < ntiles; i += 2) {
+        load_tile(key_of(i + 1), t1, lim);
+        process(t0, key_of(i));
+        load_tile(key_of(i + 2), t0, lim);
+        process(t1, key_of(i + 1));
+      }
+      if (ntiles - i == 2) {
+        load_tile(key_of(i + 1), t1, lim);
+        process(t0, key_of(i));
+        process(t1, key_of(i + 1));
+      } else {
+        process(t0, key_of(i));
+      }
+    } else if (ntiles == 2) {
+      process(t0, key_of(0));
+      process(t1, key_of(1));
     } else {
-      process(t0, key_of(i));
+      process(t0, key_of(0));
     }
   }
 
@@ -597,9 +650,7 @@ void attn_kernel(AttnArgs a) {
         sm_l[wave][c] = l_run;
       }
 #pragma unroll
-      for (int e = 0; e < CW; ++e)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm_o[wave - 1][c][CW * (4 * g4 + r) + e] = oacc[e][r];
+      for (int e = 0; e < CW; ++e) sm_o[wave - 1][e][8 * g4 + c] = oacc[e];
     }
     __syncthreads();
     if (wave > 0) return;
@@ -617,9 +668,7 @@ void attn_kernel(AttnArgs a) {
         const float fw = (M == -INFINITY || mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
         l_run += fw * sm_l[w][c];
 #pragma unroll
-        for (int e = 0; e < CW; ++e)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) oacc[e][r] += fw * sm_o[w - 1][c][CW * (4 * g4 + r) + e];
+        for (int e = 0; e < CW; ++e) oacc[e] += fw * sm_o[w - 1][e][8 * g4 + c];
       }
       m_run = M;
     }
@@ -701,7 +750,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   }
 }
 
-constexpr int kWavesPerGroup = 2;
+constexpr int kWavesPerGroup = 4;
 
 template <int D, int KIND, bool COMP>
 hipError_t launch_kind(const AttnArgs& args, int items, hipStream_t stream) {
