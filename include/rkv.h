@@ -99,7 +99,7 @@ typedef struct rkv_cfg {
 } rkv_cfg;
 
 /* Per-stream cache state (device memory, S entries, 48 bytes each).
- * Built by rkv_state_init_host and copied to the device by the caller;
+ * Built by rkv_state_init (or rkv_state_init_host and a copy by the caller);
  * afterwards only rkv_advance writes it. */
 typedef struct rkv_stream_state {
   int64_t t;          /* REBASE/COMPACT: step of the last appended token;
@@ -171,6 +171,15 @@ int rkv_validate_cfg(const rkv_cfg* cfg);
 int rkv_state_init_host(const rkv_cfg* cfg, const int32_t* h_window,
                         const int32_t* h_cap, const int64_t* h_origin,
                         rkv_stream_state* h_state);
+
+/* The same initial states as rkv_state_init_host, written to d_state[0..S)
+ * (device memory, 8-byte aligned) with copies on hip_stream.  Host arrays as
+ * above.  Blocks until the copies are done (set-up, not the per-step path);
+ * validation errors return before any HIP call, RKV_EHIP if a copy fails.
+ * Per-stream window, capacity and start: the mixed-clock pool of the Audio8
+ * model card (streams of different clocks in one batch). */
+int rkv_state_init(const rkv_cfg* cfg, rkv_stream_state* d_state, const int32_t* h_window,
+                   const int32_t* h_cap, const int64_t* h_origin, void* hip_stream);
 
 /* Bytes of workspace rkv_decode_attn / rkv_decode_step /
  * rkv_encoder_chunk_attn need for a cache of `slots` rows per head (0 when

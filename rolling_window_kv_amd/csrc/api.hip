@@ -190,6 +190,30 @@ int rkv_state_init_host(const rkv_cfg* cfg, const int32_t* h_window, const int32
   return RKV_OK;
 }
 
+int rkv_state_init(const rkv_cfg* cfg, rkv_stream_state* d_state, const int32_t* h_window,
+                   const int32_t* h_cap, const int64_t* h_origin, void* hip_stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!d_state || !h_window || !h_cap || !h_origin) return RKV_EINVAL;
+  if ((uintptr_t)d_state & 7u) return RKV_EALIGN;
+  // Built in host chunks on the stack and copied in stream order; the call
+  // returns once the copies are done, so the caller's arrays may be reused.
+  constexpr int kChunk = 128;
+  rkv_stream_state buf[kChunk];
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  rkv_cfg sub = *cfg;
+  for (int s0 = 0; s0 < cfg->num_streams; s0 += kChunk) {
+    sub.num_streams = cfg->num_streams - s0 < kChunk ? cfg->num_streams - s0 : kChunk;
+    rc = rkv_state_init_host(&sub, h_window + s0, h_cap + s0, h_origin + s0, buf);
+    if (rc) return rc;
+    hipError_t e = hipMemcpyAsync(d_state + s0, buf, sizeof(rkv_stream_state) * sub.num_streams,
+                                  hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return RKV_OK;
+}
+
 size_t rkv_workspace_bytes(const rkv_cfg* cfg, int32_t slots) {
   if (check_cfg(cfg) || slots < 1) return 0;
   return workspace_for(cfg, slots);

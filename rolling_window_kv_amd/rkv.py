@@ -36,7 +36,7 @@ RKV_MAX_HEAD_DIM = 128
 # Entry points declared in include/rkv.h (checked by the ABI tests).
 ENTRY_POINTS = (
     "rkv_version", "rkv_strerror", "rkv_last_hip_error", "rkv_validate_cfg",
-    "rkv_state_init_host", "rkv_workspace_bytes", "rkv_advance", "rkv_append",
+    "rkv_state_init_host", "rkv_state_init", "rkv_workspace_bytes", "rkv_advance", "rkv_append",
     "rkv_roll_rebase", "rkv_compact", "rkv_decode_attn", "rkv_decode_step",
     "rkv_encoder_chunk_attn",
 )
@@ -106,6 +106,7 @@ def lib():
             "rkv_last_hip_error": ([], ctypes.c_int),
             "rkv_validate_cfg": ([pc], ctypes.c_int),
             "rkv_state_init_host": ([pc, vp, vp, vp, vp], ctypes.c_int),
+            "rkv_state_init": ([pc, vp, vp, vp, vp, vp], ctypes.c_int),
             "rkv_workspace_bytes": ([pc, i32], sz),
             "rkv_advance": ([pc, vp, vp, vp], ctypes.c_int),
             "rkv_append": ([pc, vp, pk, vp, vp, vp], ctypes.c_int),
@@ -194,12 +195,26 @@ def rkv_validate_cfg(cfg) -> int:
     return lib().rkv_validate_cfg(ctypes.byref(cfg))
 
 
-def rkv_state_init_host(cfg, window, cap, origin) -> np.ndarray:
-    """Per-stream initial states as a STATE_DTYPE array (host)."""
+def _state_args(cfg, window, cap, origin):
     S = cfg.num_streams
     w = np.ascontiguousarray(np.broadcast_to(np.asarray(window, np.int32), (S,)))
     c = np.ascontiguousarray(np.broadcast_to(np.asarray(cap, np.int32), (S,)))
     o = np.ascontiguousarray(np.broadcast_to(np.asarray(origin, np.int64), (S,)))
+    return w, c, o
+
+
+def rkv_state_init(cfg, state, window, cap, origin, stream=None):
+    """Write the initial per-stream states into the device tensor `state`
+    (S * 48 bytes); returns once the copy is done."""
+    w, c, o = _state_args(cfg, window, cap, origin)
+    _check("rkv_state_init", lib().rkv_state_init(ctypes.byref(cfg), _ptr(state), w.ctypes.data,
+                                                  c.ctypes.data, o.ctypes.data, _stream(stream)))
+
+
+def rkv_state_init_host(cfg, window, cap, origin) -> np.ndarray:
+    """Per-stream initial states as a STATE_DTYPE array (host)."""
+    S = cfg.num_streams
+    w, c, o = _state_args(cfg, window, cap, origin)
     out = np.zeros(S, STATE_DTYPE)
     rc = lib().rkv_state_init_host(ctypes.byref(cfg), w.ctypes.data, c.ctypes.data,
                                    o.ctypes.data, out.ctypes.data)
@@ -294,8 +309,10 @@ class Cache:
         else:
             raise ValueError(layout)
         self.kv = kv_view(self.k, self.v, self.k_lo)
-        host = rkv_state_init_host(cfg, window, cap, origin)
-        self.state = torch.from_numpy(host.view(np.uint8).copy()).to(device)
+        self.state = torch.empty(cfg.num_streams * STATE_DTYPE.itemsize, dtype=torch.uint8,
+                                 device=device)
+        with torch.cuda.device(self.state.device):
+            rkv_state_init(cfg, self.state, window, cap, origin)
         self.plan = torch.zeros(S * PLAN_DTYPE.itemsize, dtype=torch.uint8, device=device)
         nbytes = rkv_workspace_bytes(cfg, slots)
         self.workspace = (torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=device)

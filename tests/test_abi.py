@@ -183,4 +183,16 @@ def test_calls_reject_bad_arguments_without_a_device(rkv):
                 N) == rkv.RKV_EALIGN
     assert call(rkv, "rkv_decode_step", c, F, ctypes.byref(kv), F, F, N, F, N, 0,
                 N) == rkv.RKV_EINVAL
+    # device state init: bad host arrays and mismatched streams fail before any copy
+    W = np.full(cfg.num_streams, 375, np.int32)
+    O = np.zeros(cfg.num_streams, np.int64)
+    assert call(rkv, "rkv_state_init", c, N, W.ctypes.data, W.ctypes.data, O.ctypes.data,
+                N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_state_init", c, F, N, W.ctypes.data, O.ctypes.data,
+                N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_state_init", c, ctypes.c_void_p(FAKE + 4), W.ctypes.data,
+                W.ctypes.data, O.ctypes.data, N) == rkv.RKV_EALIGN
+    W1 = W + 1
+    assert call(rkv, "rkv_state_init", c, F, W.ctypes.data, W1.ctypes.data, O.ctypes.data,
+                N) == rkv.RKV_ESTATE
     assert rkv.rkv_last_hip_error() == 0

@@ -78,3 +78,21 @@ def test_plan_encoder_ring():
     windows = np.array([750, 30, 30], np.int32)
     caps = np.array([754, 34, 40], np.int32)
     _run(rkv, cfg, windows, caps, np.array([0, 0, 8], np.int64), 260, 1, 4)
+
+
+def test_device_state_init_equals_host_build():
+    """rkv_state_init writes the same bytes as rkv_state_init_host, over more
+    streams than one host chunk (mixed windows and start offsets)."""
+    rkv = rkv_mod()
+    dev = device()
+    S = 300
+    say(f"state init: S={S}")
+    cfg = rkv.make_cfg(S, 2, rebase_chunk=25)
+    rng = np.random.default_rng(7)
+    windows = rng.choice(np.array([375, 250, 188], np.int32), S)
+    origins = rng.integers(0, 5000, S).astype(np.int64)
+    state = torch.full((S * rkv.STATE_DTYPE.itemsize,), 0xAB, dtype=torch.uint8, device=dev)
+    rkv.rkv_state_init(cfg, state, windows, windows, origins)
+    got = state.cpu().numpy()
+    ref = rkv.rkv_state_init_host(cfg, windows, windows, origins).view(np.uint8)
+    assert np.array_equal(got, ref)
