@@ -130,8 +130,9 @@ typedef struct rkv_step_plan {
   int32_t cap;
   int32_t new_rows;
   int32_t reserved[14];
-  double rope_new[RKV_MAX_NEW_ROWS][2][RKV_MAX_HEAD_DIM / 2]; /* cos, sin of (pos + j) theta_i */
-  double rope_delta[2][RKV_MAX_HEAD_DIM / 2];                 /* cos, sin of D theta_i */
+  double rope_new[RKV_MAX_NEW_ROWS][2][RKV_MAX_HEAD_DIM / 2]; /* cos, sin of (pos + j) theta_i;
+                                                                written for j < new_rows, i < d/2 */
+  double rope_delta[2][RKV_MAX_HEAD_DIM / 2];                 /* cos, sin of D theta_i, i < d/2 */
 } rkv_step_plan;
 
 /* Where the cache lives (host struct describing device memory).

@@ -15,8 +15,8 @@
 //   max(origin, P - W).
 //
 // One block of 64 threads per stream.  All threads derive the integer plan
-// from the old state; thread 0 publishes plan and new state; thread i fills
-// the rotary tables of pair i (angles, cosines and sines in float64).
+// from the old state; thread 0 publishes plan and new state; thread i < d/2
+// fills the rotary tables of pair i (angles, cosines and sines in float64).
 
 #include <math.h>
 
@@ -127,17 +127,19 @@ __global__ __launch_bounds__(64) void advance_kernel(rkv_stream_state* __restric
     out->new_rows = p.new_rows;
     for (int r = 0; r < 14; ++r) out->reserved[r] = 0;
   }
-  const bool live = i < half;
-  const double theta = live ? th.v[i] : 0.0;
+  // Only the rows and pairs a step uses are written (rows j < new_rows,
+  // pairs i < d/2); a zero delta has the exact table cos = 1, sin = 0.
+  if (i >= half) return;
+  const double theta = th.v[i];
 #pragma unroll 1
-  for (int j = 0; j < RKV_MAX_NEW_ROWS; ++j) {
-    double sn = 0.0, cs = 0.0;
-    if (live && j < p.new_rows) sincos((double)(p.pos + j) * theta, &sn, &cs);
+  for (int j = 0; j < p.new_rows; ++j) {
+    double sn, cs;
+    sincos((double)(p.pos + j) * theta, &sn, &cs);
     out->rope_new[j][0][i] = cs;
     out->rope_new[j][1][i] = sn;
   }
-  double sn = 0.0, cs = 0.0;
-  if (live) sincos((double)p.delta * theta, &sn, &cs);
+  double sn = 0.0, cs = 1.0;
+  if (p.delta != 0) sincos((double)p.delta * theta, &sn, &cs);
   out->rope_delta[0][i] = cs;
   out->rope_delta[1][i] = sn;
 }
