@@ -208,6 +208,10 @@ int rkv_append(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
  * streams whose plan has rebase_delta D > 0, every retained K row (rows
  * [0, n_valid) except the new row's slot) becomes rne(R(-D) K) in place
  * (compensated: x = K + k_lo, K = rne(R(-D) x), k_lo = rne(R(-D) x - K)).
+ * The rotation is an exact rotation matrix evaluated in float32 (cos/sin
+ * rounded from the plan's float64 tables), each result rounded to nearest
+ * bfloat16: within 1 ulp of the correctly rounded value, and bit-identical to
+ * the re-base inside rkv_decode_step.
  * REBASE mode only; call after rkv_advance and before rkv_append. */
 int rkv_roll_rebase(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
                     const rkv_kv_view* kv, void* hip_stream);

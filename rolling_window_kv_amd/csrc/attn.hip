@@ -43,10 +43,14 @@
 // float64 (one rotary chunk pair each), write K and V to the ring and leave
 // both in LDS, from where the wave whose tile holds the new slot patches them
 // into its registers (its tile may have been read before the write).  In
-// REBASE mode, when the plan's delta D > 0, each wave first rotates every other
-// retained row of its own tiles by R(-D) in float64, writes it back (exact
-// re-base) and reads its first tiles again.  Encoder: each wave writes the new
-// frames that fall in its own tiles before reading them.
+// REBASE mode, when the plan's delta D > 0, each wave re-bases the rows of its
+// tiles in registers as they arrive (R(-D) in float32 with hi/lo tables and
+// exact product errors, rounded to bfloat16: the arithmetic of rkv_roll_rebase)
+// and writes them back, so K is read once.
+// Encoder: each wave writes the new frames that fall in its own tiles before
+// reading them.
+
+#include <type_traits>
 
 #include "rkv_device.h"
 #include "rkv_internal.h"
@@ -88,7 +92,6 @@ struct VChunk<4> {
 };
 
 constexpr float kLazyMax = 8.0f;  // rescale only when the max grows by > 2^8
-constexpr bool INLOOP = false;    // fused updates on the tiles in registers (else a pre-pass)
 
 // Waves per SIMD the register allocation targets: the largest count that
 // fits without spilling (the compensated re-base keeps two more K arrays live).
@@ -114,6 +117,7 @@ void attn_kernel(AttnArgs a) {
   __shared__ float sm_m[NW][8];
   __shared__ float sm_l[NW][8];
   __shared__ f32x4 sm_o[NW > 1 ? NW - 1 : 1][CW][32];  // [wave-1][e][8*g4 + c], c < 8
+  __shared__ f32x4 sm_dt[D / 2];  // re-base: hi/lo float32 of cos(D theta_i), -sin(D theta_i)
 
   const int lane = threadIdx.x & 63;
   // wave index made provably uniform, so tile-index branches are scalar
@@ -154,9 +158,12 @@ void attn_kernel(AttnArgs a) {
     return (((int64_t)l * a.S + s) * a.Hkv + g) * D;
   };
 
+  // The compensated decoder also carries the K residual chunks of its rows.
+  constexpr bool LO = COMP && KIND == kDecodeFused;
   struct Tile {
     u32x4 k[KS];
     VT v[4];
+    u32x4 lo[LO ? KS : 1];
   };
   // Rows past `lim` (the last row that may be read) are clamped to it, so a
   // partial tile reads valid data; its masked keys get probability 0.
@@ -169,6 +176,10 @@ void attn_kernel(AttnArgs a) {
       const int rv0 = key0 + 4 * g4 + j;
       const int rv = rv0 < lim ? rv0 : lim;
       T.v[j] = VC::load(Vp + rv * rs + CW * c);
+    }
+    if (LO) {
+#pragma unroll
+      for (int st = 0; st < KS; ++st) T.lo[st] = ld16(Lp + rk * rs + 32 * st + 8 * g4);
     }
   };
 
@@ -316,7 +327,7 @@ void attn_kernel(AttnArgs a) {
   // Decoder RoPE-on-append: the waves rotate the new K row (float64,
   // correctly rounded) chunk pair by chunk pair, write K and V to the ring and
   // leave both in LDS for the wave whose tile holds the new slot.
-  if (KIND == kDecodeFused && !INLOOP) {
+  if (KIND == kDecodeFused) {
 #pragma unroll
     for (int k = 0; k < QST; ++k) {
       const int st = wave + NW * k;
@@ -358,96 +369,14 @@ void attn_kernel(AttnArgs a) {
     }
   }
 
-  // ---- fused cache updates: a pre-pass over this wave's own tiles ----
   auto key_of = [&](int i) { return first + TK * NW * i; };
   const int ntiles = first < ke ? (ke - first + TK * NW - 1) / (TK * NW) : 0;
   const int lim0 = ke > 0 ? ke - 1 : 0;  // last readable row of the valid range
-  if (KIND != kDecodeRead && !INLOOP) {
-    // (1) Exact re-base of every retained row of the wave's tiles when the
-    // base moved (delta != 0).  The lane's cos/sin(delta theta_i) stay in
-    // registers and the next tile's rows load while the current one rotates.
-    if (KIND == kDecodeFused && delta != 0) {
-      // one pass per chunk pair (st, st + KH): 8 rotary pairs' tables live
-      for (int st = 0; st < KH; ++st) {
-        double dcs[8], dsn[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 32 * st + 8 * g4 + e;
-          dcs[e] = P->rope_delta[0][i];
-          dsn[e] = -P->rope_delta[1][i];
-        }
-        const int o1 = 32 * st + 8 * g4, o2 = 32 * (st + KH) + 8 * g4;
-        auto ldrow = [&](int i, u32x4* k) {
-          const int row = key_of(i) + c < ke ? key_of(i) + c : ke - 1;
-          k[0] = ld16(Kp + row * rs + o1);
-          k[1] = ld16(Kp + row * rs + o2);
-          if (COMP) {
-            k[2] = ld16(Lp + row * rs + o1);
-            k[3] = ld16(Lp + row * rs + o2);
-          }
-        };
-        auto rebase_row = [&](int i, const u32x4* k) {
-          const int row = key_of(i) + c;
-          if (row >= ke || new_index(row) >= 0) return;
-          u32x4 w1, w2, r1, r2;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            double y1[2], y2[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int e = 2 * w + h;
-              double x1 = bf2f(elem8(k[0], e)), x2 = bf2f(elem8(k[1], e));
-              if (COMP) {
-                x1 += (double)bf2f(elem8(k[2], e));
-                x2 += (double)bf2f(elem8(k[3], e));
-              }
-              rotate_pair64(x1, x2, dcs[e], dsn[e], y1[h], y2[h]);
-            }
-            w1[w] = cvt2_bf16_f64(y1[0], y1[1]);
-            w2[w] = cvt2_bf16_f64(y2[0], y2[1]);
-            if (COMP) {
-              r1[w] = cvt2_bf16_f64(y1[0] - (double)bf2f(w1[w] & 0xffffu),
-                                    y1[1] - (double)bf2f(w1[w] >> 16));
-              r2[w] = cvt2_bf16_f64(y2[0] - (double)bf2f(w2[w] & 0xffffu),
-                                    y2[1] - (double)bf2f(w2[w] >> 16));
-            }
-          }
-          st16(Kp + row * rs + o1, w1);
-          st16(Kp + row * rs + o2, w2);
-          if (COMP) {
-            st16(Lp + row * rs + o1, r1);
-            st16(Lp + row * rs + o2, r2);
-          }
-        };
-        if (ntiles > 0) {
-          u32x4 ka[4], kb2[4];
-          ldrow(0, ka);
-          int i = 0;
-          for (; i + 2 < ntiles; i += 2) {
-            ldrow(i + 1, kb2);
-            rebase_row(i, ka);
-            ldrow(i + 2, ka);
-            rebase_row(i + 1, kb2);
-          }
-          if (ntiles - i == 2) {
-            ldrow(i + 1, kb2);
-            rebase_row(i, ka);
-            rebase_row(i + 1, kb2);
-          } else {
-            rebase_row(i, ka);
-          }
-        }
-      }
-      // the early tiles are stale: read the re-based rows back
-      load_tile(first, tb[0], lim0);
-      load_tile(key_of(1), tb[1], lim0);
-    }
-    // (2) Encoder: RoPE-on-append of the new frames that fall in the wave's tiles.
-    for (int tt = 0; KIND == kEncoderFused && tt < ntiles; ++tt) {
+  // Encoder RoPE-on-append: each wave writes the new frames that fall in its
+  // own tiles (float64, correctly rounded) and reads those tiles again.
+  if (KIND == kEncoderFused) {
+    for (int tt = 0; tt < ntiles; ++tt) {
       const int key0 = key_of(tt);
-      bool any_new = true;
-      if (KIND == kDecodeFused) any_new = slot_new >= key0 && slot_new < key0 + TK;
-      if (!any_new) continue;
       const int row = key0 + c;
       if (row < ke) {
         const int jn = new_index(row);
@@ -467,17 +396,17 @@ void attn_kernel(AttnArgs a) {
         if (jn >= 0) VC::store(Vp + rv * rs + CW * c, VC::load(a.vnew + new_off(jn) + CW * c));
       }
     }
-    if (KIND == kEncoderFused) {
-      // the early tiles are stale: read the appended rows back
-      load_tile(first, tb[0], lim0);
-      load_tile(key_of(1), tb[1], lim0);
-    }
+    load_tile(first, tb[0], lim0);
+    load_tile(key_of(1), tb[1], lim0);
+  }
+
+  // Re-base tables for the in-loop rotation (float32, from the float64 plan).
+  if (KIND == kDecodeFused && delta != 0 && wave == 0) {
+    for (int i = lane; i < D / 2; i += 64)
+      sm_dt[i] = rebase_table_entry(P->rope_delta[0][i], P->rope_delta[1][i]);
   }
 
   __syncthreads();  // the query operand (and the decoder's new row) is in LDS
-  bf16x8 qop[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) qop[st] = __builtin_bit_cast(bf16x8, sm_q[st][lane]);
 
   // encoder mask bookkeeping
   const int64_t last_pos = P->t;
@@ -491,8 +420,33 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < CW; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](Tile& T, int key0) {
-    if (KIND == kDecodeFused && !INLOOP && slot_new >= key0 && slot_new < key0 + TK) {
+  // reb: std::integral_constant<bool, re-base this launch's tiles>
+  auto process = [&](Tile& T, int key0, auto reb) __attribute__((always_inline)) {
+    if (KIND == kDecodeFused && decltype(reb)::value && delta != 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      // Exact re-base of the tile's rows in registers (R(-D), float32, rounded
+      // to nearest bfloat16), written back for every valid row but the new
+      // one, whose slot receives the appended row.
+      const int row = key0 + c;
+#pragma unroll
+      for (int st = 0; st < KH; ++st) {
+        const int i0 = 32 * st + 8 * g4;
+        u32x4 dl = u32x4{0u, 0u, 0u, 0u}, dh = dl;
+        rebase_chunks_ff<LO>(T.k[st], T.k[st + KH], LO ? T.lo[st % (LO ? KS : 1)] : dl,
+                             LO ? T.lo[(st + KH) % (LO ? KS : 1)] : dh,
+                             [&](int e) { return sm_dt[i0 + e]; });
+      }
+      if (row < ke && row != slot_new) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          st16(Kp + row * rs + 32 * st + 8 * g4, T.k[st]);
+          if (LO) st16(Lp + row * rs + 32 * st + 8 * g4, T.lo[st % (LO ? KS : 1)]);
+        }
+      }
+      // keep the re-base and the attention math apart (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (KIND == kDecodeFused && slot_new >= key0 && slot_new < key0 + TK) {
       // the new row lies in this tile: take its rotated K and V from LDS
       const int r = slot_new - key0;
       if (c == r) {
@@ -505,43 +459,11 @@ void attn_kernel(AttnArgs a) {
           if (j == (r & 3)) T.v[j] = sm_newv[c];
       }
     }
-    if (KIND != kDecodeRead && INLOOP) {
-      // fused updates on the tile already in registers
-      const int row = key0 + c;
-      if (row < ke) {
-        const int jn = new_index(row);
-        if (jn >= 0) {
-          u32x4 src[KS];
-          const uint16_t* kn = a.knew + new_off(jn);
-#pragma unroll
-          for (int st = 0; st < KS; ++st) src[st] = ld16(kn + 32 * st + 8 * g4);
-          rotate_row(src, nullptr, P->rope_new[jn][0], P->rope_new[jn][1], 1.0, row, T.k);
-        } else if (delta != 0) {
-          u32x4 src[KS], lo[KS];
-#pragma unroll
-          for (int st = 0; st < KS; ++st) {
-            src[st] = T.k[st];
-            lo[st] = COMP ? ld16(Lp + row * rs + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
-          }
-          rotate_row(src, COMP ? lo : nullptr, P->rope_delta[0], P->rope_delta[1], -1.0, row,
-                     T.k);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rv = key0 + 4 * g4 + j;
-        if (rv >= ke) continue;
-        const int jn = new_index(rv);
-        if (jn >= 0) {
-          T.v[j] = VC::load(a.vnew + new_off(jn) + CW * c);
-          VC::store(Vp + rv * rs + CW * c, T.v[j]);
-        }
-      }
-    }
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < KS; ++st)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[st]), qop[st],
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[st]),
+                                                    __builtin_bit_cast(bf16x8, sm_q[st][lane]),
                                                     acc, 0, 0, 0);
     float sv[4];
     float mx = -INFINITY;
@@ -603,36 +525,37 @@ void attn_kernel(AttnArgs a) {
   // the compiler keeps the next tile's loads in flight across the current
   // tile's math (a conditional load makes it wait for every outstanding load).
   const int lim = lim0;
-  if (ntiles > 0) {
+  auto run_tiles = [&](auto reb) __attribute__((always_inline)) {
     Tile& t0 = tb[0];
     Tile& t1 = tb[1];
     // tiles 0 and 1 are already in flight
     int i = 0;
     if (ntiles > 2) {
-      process(t0, key_of(0));
+      process(t0, key_of(0), reb);
       load_tile(key_of(2), t0, lim);
-      process(t1, key_of(1));
+      process(t1, key_of(1), reb);
       i = 2;
       for (; i + 2 < ntiles; i += 2) {
         load_tile(key_of(i + 1), t1, lim);
-        process(t0, key_of(i));
+        process(t0, key_of(i), reb);
         load_tile(key_of(i + 2), t0, lim);
-        process(t1, key_of(i + 1));
+        process(t1, key_of(i + 1), reb);
       }
       if (ntiles - i == 2) {
         load_tile(key_of(i + 1), t1, lim);
-        process(t0, key_of(i));
-        process(t1, key_of(i + 1));
+        process(t0, key_of(i), reb);
+        process(t1, key_of(i + 1), reb);
       } else {
-        process(t0, key_of(i));
+        process(t0, key_of(i), reb);
       }
     } else if (ntiles == 2) {
-      process(t0, key_of(0));
-      process(t1, key_of(1));
+      process(t0, key_of(0), reb);
+      process(t1, key_of(1), reb);
     } else {
-      process(t0, key_of(0));
+      process(t0, key_of(0), reb);
     }
-  }
+  };
+  if (ntiles > 0) run_tiles(std::integral_constant<bool, true>());
 
   // ---- per-wave reduction: row sums over lane groups, hi+lo columns ----
   l_run += __shfl_xor(l_run, 16);

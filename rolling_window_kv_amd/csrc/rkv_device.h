@@ -90,6 +90,78 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
   return w;
 }
 
+// Rotation of one pair by an angle whose cosine and sine are given as float32
+// hi + lo pairs (c = ch + cl, s = sh + sl): y1 = x1 c - x2 s, y2 = x1 s + x2 c
+// for float32 inputs x1, x2 with at most 16 significant bits.  The rounding
+// error of each large product is recovered exactly with an fma and added back
+// with the small terms, so the error is about 2^-24 of the result itself
+// rather than of the products: under cancellation the result keeps its
+// accuracy, and rounding it to bfloat16 lands within 1 ulp of the correctly
+// rounded rotation.
+__device__ __forceinline__ void rotate_pair_ff(float x1, float x2, float ch, float cl, float sh,
+                                               float sl, float& y1, float& y2) {
+  const float p1 = x2 * sh;
+  const float e1 = fmaf(x2, sh, -p1);             // x2 sh = p1 + e1 exactly
+  const float h1 = fmaf(x1, ch, -p1);             // x1 ch - p1, rounded once
+  const float t1 = fmaf(x1, cl, -fmaf(x2, sl, e1));
+  y1 = h1 + t1;
+  const float p2 = x2 * ch;
+  const float e2 = fmaf(x2, ch, -p2);             // x2 ch = p2 + e2 exactly
+  const float h2 = fmaf(x1, sh, p2);              // x1 sh + p2, rounded once
+  const float t2 = fmaf(x1, sl, fmaf(x2, cl, e2));
+  y2 = h2 + t2;
+}
+
+// Re-base one chunk pair of a K row by R(-D): a holds dims i0 .. i0+7 and b
+// dims i0 + d/2 .. (the rotary partners); table(e) returns {ch, cl, sh, sl} of
+// pair i0 + e, the float32 hi/lo split of cos(D theta) and -sin(D theta).
+// Inputs are exact in float32 (bfloat16, or hi + lo with at most 16
+// significant bits); each result is rounded to nearest bfloat16.
+// Compensated: la / lb hold the residuals; x = hi + lo is rotated and split
+// again into hi and lo.
+template <bool COMP, typename Table>
+__device__ __forceinline__ void rebase_chunks_ff(u32x4& a, u32x4& b, u32x4& la, u32x4& lb,
+                                                 Table table) {
+  u32x4 na, nb, nla, nlb;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float y1[2], y2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * w + h;
+      const int sh = 16 * h;
+      float x1 = __uint_as_float(((a[w] >> sh) & 0xffffu) << 16);
+      float x2 = __uint_as_float(((b[w] >> sh) & 0xffffu) << 16);
+      if (COMP) {
+        x1 += __uint_as_float(((la[w] >> sh) & 0xffffu) << 16);
+        x2 += __uint_as_float(((lb[w] >> sh) & 0xffffu) << 16);
+      }
+      const f32x4 t = table(e);
+      rotate_pair_ff(x1, x2, t[0], t[1], t[2], t[3], y1[h], y2[h]);
+    }
+    na[w] = cvt2_bf16(y1[0], y1[1]);
+    nb[w] = cvt2_bf16(y2[0], y2[1]);
+    if (COMP) {
+      nla[w] = cvt2_bf16(y1[0] - bf2f(na[w] & 0xffffu), y1[1] - bf2f(na[w] >> 16));
+      nlb[w] = cvt2_bf16(y2[0] - bf2f(nb[w] & 0xffffu), y2[1] - bf2f(nb[w] >> 16));
+    }
+  }
+  a = na;
+  b = nb;
+  if (COMP) {
+    la = nla;
+    lb = nlb;
+  }
+}
+
+// {ch, cl, sh, sl}: float32 hi/lo split of c = cos(x) and -s = -sin(x) for
+// rebase_chunks_ff.
+__device__ __forceinline__ f32x4 rebase_table_entry(double c, double s) {
+  const float ch = (float)c;
+  const float sh = (float)(-s);
+  return f32x4{ch, (float)(c - (double)ch), sh, (float)(-s - (double)sh)};
+}
+
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

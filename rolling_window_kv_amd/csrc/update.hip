@@ -55,8 +55,10 @@ __global__ __launch_bounds__(64) void append_kernel(const rkv_step_plan* __restr
 
 // ---------------------------------------------------------------------------
 // Exact re-base (Audio8 explainer, "Rolling KV Cache 三步拆解" step 2): every
-// retained K row is rotated by R(-D) in place.  A thread owns 8 rotary pairs
-// of one row: 16 bytes from each half of the row.
+// retained K row is rotated by R(-D) in place (float32 with hi/lo tables and
+// exact product errors, rounded to nearest bfloat16: within 1 ulp of the
+// correctly rounded rotation; the same arithmetic as the fused decode step).  A thread
+// owns 8 rotary pairs of one row: 16 bytes from each half of the row.
 // ---------------------------------------------------------------------------
 template <int D, bool COMP>
 __global__ __launch_bounds__(256) void rebase_kernel(const rkv_step_plan* __restrict__ plan,
@@ -76,45 +78,20 @@ __global__ __launch_bounds__(256) void rebase_kernel(const rkv_step_plan* __rest
                       (int64_t)r * ring.rs;
   uint16_t* k1 = ring.k + row + 8 * c;
   uint16_t* k2 = k1 + HALF;
-  const u32x4 a = ld16(k1), b = ld16(k2);
+  u32x4 a = ld16(k1), b = ld16(k2);
   u32x4 la = {0u, 0u, 0u, 0u}, lb = {0u, 0u, 0u, 0u};
   if (COMP) {
     la = ld16(ring.klo + row + 8 * c);
     lb = ld16(ring.klo + row + 8 * c + HALF);
   }
-  u32x4 ha, hb, ra, rb;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t wa = 0, wb = 0, wla = 0, wlb = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = 2 * w + h;
-      const int i = 8 * c + e;
-      double x1 = bf2f(elem8(a, e)), x2 = bf2f(elem8(b, e));
-      if (COMP) {
-        x1 += (double)bf2f(elem8(la, e));
-        x2 += (double)bf2f(elem8(lb, e));
-      }
-      double y1, y2;
-      rotate_pair64(x1, x2, P->rope_delta[0][i], -P->rope_delta[1][i], y1, y2);
-      const uint32_t h1 = f64_to_bf16(y1), h2 = f64_to_bf16(y2);
-      wa |= h1 << (16 * h);
-      wb |= h2 << (16 * h);
-      if (COMP) {
-        wla |= f64_to_bf16(y1 - (double)bf2f(h1)) << (16 * h);
-        wlb |= f64_to_bf16(y2 - (double)bf2f(h2)) << (16 * h);
-      }
-    }
-    ha[w] = wa;
-    hb[w] = wb;
-    ra[w] = wla;
-    rb[w] = wlb;
-  }
-  st16(k1, ha);
-  st16(k2, hb);
+  rebase_chunks_ff<COMP>(a, b, la, lb, [&](int e) {
+    return rebase_table_entry(P->rope_delta[0][8 * c + e], P->rope_delta[1][8 * c + e]);
+  });
+  st16(k1, a);
+  st16(k2, b);
   if (COMP) {
-    st16(ring.klo + row + 8 * c, ra);
-    st16(ring.klo + row + 8 * c + HALF, rb);
+    st16(ring.klo + row + 8 * c, la);
+    st16(ring.klo + row + 8 * c + HALF, lb);
   }
 }
 
