@@ -57,41 +57,46 @@ __global__ __launch_bounds__(64) void append_kernel(const rkv_step_plan* __restr
 // Exact re-base (Audio8 explainer, "Rolling KV Cache 三步拆解" step 2): every
 // retained K row is rotated by R(-D) in place (float32 with hi/lo tables and
 // exact product errors, rounded to nearest bfloat16: within 1 ulp of the
-// correctly rounded rotation; the same arithmetic as the fused decode step).  A thread
-// owns 8 rotary pairs of one row: 16 bytes from each half of the row.
+// correctly rounded rotation; the same arithmetic as the fused decode step).
+// One block per (layer, stream, head) item; a thread owns 8 rotary pairs of a
+// row (16 bytes from each half) and walks the item's rows.
 // ---------------------------------------------------------------------------
 template <int D, bool COMP>
 __global__ __launch_bounds__(256) void rebase_kernel(const rkv_step_plan* __restrict__ plan,
                                                      RingArgs ring, int S, int H) {
   constexpr int HALF = D / 2;
   constexpr int TPR = HALF / 8;       // threads per row
-  constexpr int RPB = 256 / TPR;      // rows per block
+  constexpr int RPB = 256 / TPR;      // rows per pass of the block
   int l, s, g;
   item_coords(blockIdx.x, H, S, l, s, g);
   const rkv_step_plan* P = plan + s;
-  if (P->rebase_delta == 0) return;
-  const int r = blockIdx.y * RPB + threadIdx.x / TPR;
+  if (P->rebase_delta == 0) return;   // most steps: the whole item is untouched
   const int c = threadIdx.x % TPR;
   const int n_valid = P->n_valid < ring.slots ? P->n_valid : ring.slots;
-  if (r >= n_valid || r == P->slot) return;
-  const int64_t row = (int64_t)l * ring.ls + (int64_t)s * ring.ss + (int64_t)g * ring.hs +
-                      (int64_t)r * ring.rs;
-  uint16_t* k1 = ring.k + row + 8 * c;
-  uint16_t* k2 = k1 + HALF;
-  u32x4 a = ld16(k1), b = ld16(k2);
-  u32x4 la = {0u, 0u, 0u, 0u}, lb = {0u, 0u, 0u, 0u};
-  if (COMP) {
-    la = ld16(ring.klo + row + 8 * c);
-    lb = ld16(ring.klo + row + 8 * c + HALF);
-  }
-  rebase_chunks_ff<COMP>(a, b, la, lb, [&](int e) {
-    return rebase_table_entry(P->rope_delta[0][8 * c + e], P->rope_delta[1][8 * c + e]);
-  });
-  st16(k1, a);
-  st16(k2, b);
-  if (COMP) {
-    st16(ring.klo + row + 8 * c, la);
-    st16(ring.klo + row + 8 * c + HALF, lb);
+  const int skip = P->slot;
+  f32x4 tab[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    tab[e] = rebase_table_entry(P->rope_delta[0][8 * c + e], P->rope_delta[1][8 * c + e]);
+  const int64_t base = (int64_t)l * ring.ls + (int64_t)s * ring.ss + (int64_t)g * ring.hs;
+  for (int r = threadIdx.x / TPR; r < n_valid; r += RPB) {
+    if (r == skip) continue;
+    const int64_t row = base + (int64_t)r * ring.rs;
+    uint16_t* k1 = ring.k + row + 8 * c;
+    uint16_t* k2 = k1 + HALF;
+    u32x4 a = ld16(k1), b = ld16(k2);
+    u32x4 la = {0u, 0u, 0u, 0u}, lb = {0u, 0u, 0u, 0u};
+    if (COMP) {
+      la = ld16(ring.klo + row + 8 * c);
+      lb = ld16(ring.klo + row + 8 * c + HALF);
+    }
+    rebase_chunks_ff<COMP>(a, b, la, lb, [&](int e) { return tab[e]; });
+    st16(k1, a);
+    st16(k2, b);
+    if (COMP) {
+      st16(ring.klo + row + 8 * c, la);
+      st16(ring.klo + row + 8 * c + HALF, lb);
+    }
   }
 }
 
@@ -166,8 +171,7 @@ hipError_t launch_rebase(const rkv_cfg* cfg, const rkv_step_plan* plan, const Ri
                          hipStream_t stream) {
   const int S = cfg->num_streams, H = cfg->num_kv_heads, L = cfg->num_layers;
   const bool comp = (cfg->flags & RKV_F_COMPENSATED) != 0;
-  const int rpb = 256 / (cfg->head_dim / 16);
-  const dim3 grid(L * S * H, (ring.slots + rpb - 1) / rpb);
+  const dim3 grid(L * S * H);
   if (cfg->head_dim == 128) {
     if (comp) hipLaunchKernelGGL((rebase_kernel<128, true>), grid, dim3(256), 0, stream, plan, ring, S, H);
     else hipLaunchKernelGGL((rebase_kernel<128, false>), grid, dim3(256), 0, stream, plan, ring, S, H);
