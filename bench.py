@@ -244,8 +244,24 @@ def run_gpu(c, args):
     ws = cache.workspace
     separate = args.path == "separate"
 
+    pipelined = args.path == "pipelined" and c["mode"] != "enc"
+    plans = [cache.plan, cache.plan_next]
+
     def step(i, ev=None):
         j = i % P
+        if pipelined:
+            # one launch per step: this step's plan was written by the previous
+            # launch (or the priming rkv_advance), the next one is written now
+            cur, nxt = plans[i % 2], plans[(i + 1) % 2]
+            if c["mode"] == "compact":
+                rkv.rkv_compact(cfg, cur, cache.kv, sp)
+            if ev is not None:
+                ev[0].record(stream)
+            rkv.rkv_decode_step_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[j], k[j],
+                                          v[j], out, ws, sp)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         rkv.rkv_advance(cfg, cache.state, cache.plan, sp)
         if c["mode"] == "compact":
             rkv.rkv_compact(cfg, cache.plan, cache.kv, sp)
@@ -282,6 +298,8 @@ def run_gpu(c, args):
         else:
             fill(i)
         i += 1
+    if pipelined:                     # the first pipelined step's plan
+        rkv.rkv_advance(cfg, cache.state, plans[i % 2], sp)
     for _ in range(args.warmup):
         step(i)
         i += 1
@@ -362,9 +380,12 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS))
-    ap.add_argument("--path", choices=("fused", "separate"), default="fused",
-                    help="fused: rkv_decode_step; separate: rkv_roll_rebase + rkv_append + "
-                         "rkv_decode_attn")
+    ap.add_argument("--path", choices=("pipelined", "fused", "separate"), default="pipelined",
+                    help="pipelined: rkv_decode_step_pipelined (the step plan of the next "
+                         "step computed in the same launch); fused: rkv_advance + "
+                         "rkv_decode_step; separate: rkv_advance + rkv_roll_rebase + "
+                         "rkv_append + rkv_decode_attn (encoder workloads: always "
+                         "rkv_advance + rkv_encoder_chunk_attn)")
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     ap.add_argument("--cpu-budget", type=float, default=15.0)

@@ -242,6 +242,23 @@ int rkv_decode_step(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
                     const void* v_new, void* out, void* workspace,
                     size_t workspace_bytes, void* hip_stream);
 
+/* Pipelined decode step for callers that keep two plan buffers: the decode
+ * step of rkv_decode_step with d_plan, and in the same launch the next step's
+ * plan written to d_plan_next with d_state advanced, exactly what
+ * rkv_advance(d_state, d_plan_next) would write.  The sequence
+ *   rkv_advance(state, A); pipelined(state, A, B); pipelined(state, B, A); ...
+ * gives bit-identical rings, outputs, states and plans to rkv_advance +
+ * rkv_decode_step per step, with one launch per step instead of two (the
+ * plan of the Audio8 explainer's "Rolling KV Cache 三步拆解" steps 1-2 is
+ * only needed by the next step).  d_plan and d_plan_next must not overlap
+ * (RKV_EINVAL); d_state 8-byte and d_plan_next 16-byte aligned.  In
+ * COMPACT mode call rkv_compact with d_plan first, as for rkv_decode_step. */
+int rkv_decode_step_pipelined(const rkv_cfg* cfg, rkv_stream_state* d_state,
+                              const rkv_step_plan* d_plan, rkv_step_plan* d_plan_next,
+                              const rkv_kv_view* kv, const void* q, const void* k_new,
+                              const void* v_new, void* out, void* workspace,
+                              size_t workspace_bytes, void* hip_stream);
+
 /* Encoder chunk attention (voxtral.c explainer section 三: only the new
  * positions are computed, against the cached K/V of the window).  Appends the
  * F frames of the chunk (as rkv_append) and computes, for every head and frame

@@ -96,9 +96,18 @@ size_t workspace_for(const rkv_cfg* c, int32_t slots) {
 
 int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
               const rkv_kv_view* kv, const void* q, const void* knew, const void* vnew,
-              void* out, void* ws, size_t ws_bytes, void* stream) {
+              void* out, void* ws, size_t ws_bytes, void* stream,
+              rkv_stream_state* next_state = nullptr, rkv_step_plan* next_plan = nullptr) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
+  if (next_state || next_plan) {
+    if (!next_state || !next_plan || !plan) return RKV_EINVAL;
+    if (((uintptr_t)next_state & 7u) || !aligned16(next_plan)) return RKV_EALIGN;
+    // the plan being read and the plan being written must not overlap
+    const uintptr_t a0 = (uintptr_t)plan, b0 = (uintptr_t)next_plan;
+    const uintptr_t n = sizeof(rkv_step_plan) * (uintptr_t)cfg->num_streams;
+    if (a0 < b0 + n && b0 < a0 + n) return RKV_EINVAL;
+  }
   if (kind == rkv::kEncoderFused && cfg->mode != RKV_MODE_ENC_CHUNK) return RKV_EINVAL;
   if (kind != rkv::kEncoderFused && cfg->mode == RKV_MODE_ENC_CHUNK) return RKV_EINVAL;
   if ((rc = check_kv(cfg, kv))) return rc;
@@ -128,6 +137,13 @@ int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
   const double scale =
       cfg->softmax_scale > 0.0f ? (double)cfg->softmax_scale : 1.0 / sqrt((double)cfg->head_dim);
   a.scale_log2 = (float)(scale * 1.4426950408889634);
+  a.adv_state = next_state;
+  a.adv_plan = next_plan;
+  a.adv_mode = cfg->mode;
+  a.adv_dc = cfg->rebase_chunk;
+  a.adv_F = cfg->new_rows;
+  a.adv_half = cfg->head_dim / 2;
+  a.adv_theta = rkv::theta_table(cfg);
   return hip_status(rkv::launch_attention(cfg, kind, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -272,6 +288,15 @@ int rkv_decode_step(const rkv_cfg* cfg, const rkv_step_plan* d_plan, const rkv_k
                     void* workspace, size_t workspace_bytes, void* hip_stream) {
   return attention(cfg, rkv::kDecodeFused, d_plan, kv, q, k_new, v_new, out, workspace,
                    workspace_bytes, hip_stream);
+}
+
+int rkv_decode_step_pipelined(const rkv_cfg* cfg, rkv_stream_state* d_state,
+                              const rkv_step_plan* d_plan, rkv_step_plan* d_plan_next,
+                              const rkv_kv_view* kv, const void* q, const void* k_new,
+                              const void* v_new, void* out, void* workspace,
+                              size_t workspace_bytes, void* hip_stream) {
+  return attention(cfg, rkv::kDecodeFused, d_plan, kv, q, k_new, v_new, out, workspace,
+                   workspace_bytes, hip_stream, d_state, d_plan_next);
 }
 
 int rkv_encoder_chunk_attn(const rkv_cfg* cfg, const rkv_step_plan* d_plan,

@@ -119,6 +119,19 @@ void attn_kernel(AttnArgs a) {
   __shared__ f32x4 sm_o[NW > 1 ? NW - 1 : 1][CW][32];  // [wave-1][e][8*g4 + c], c < 8
   __shared__ f32x4 sm_dt[D / 2];  // re-base: hi/lo float32 of cos(D theta_i), -sin(D theta_i)
 
+  // Pipelined decode step: the blocks past the attention grid compute the
+  // next step's plan, one wave per stream (nothing in this launch reads it).
+  if (KIND == kDecodeFused && a.adv_state) {
+    const int njobs = a.L * a.S * a.Hkv * a.nsplit;
+    if ((int)blockIdx.x >= njobs) {
+      const int s = ((int)blockIdx.x - njobs) * NW + (int)(threadIdx.x >> 6);
+      if (s < a.S)
+        advance_stream(a.adv_state, a.adv_plan, s, threadIdx.x & 63, a.adv_mode, a.adv_dc,
+                       a.adv_F, a.adv_half, a.adv_theta);
+      return;
+    }
+  }
+
   const int lane = threadIdx.x & 63;
   // wave index made provably uniform, so tile-index branches are scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -677,8 +690,10 @@ constexpr int kWavesPerGroup = 4;
 
 template <int D, int KIND, bool COMP>
 hipError_t launch_kind(const AttnArgs& args, int items, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_kernel<D, kWavesPerGroup, KIND, COMP>), dim3(items * args.nsplit),
-                     dim3(kWavesPerGroup * 64), 0, stream, args);
+  const int extra = args.adv_state ? (args.S + kWavesPerGroup - 1) / kWavesPerGroup : 0;
+  hipLaunchKernelGGL((attn_kernel<D, kWavesPerGroup, KIND, COMP>),
+                     dim3(items * args.nsplit + extra), dim3(kWavesPerGroup * 64), 0, stream,
+                     args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || args.nsplit == 1) return e;
   hipLaunchKernelGGL((combine_kernel<D, KIND>), dim3(items), dim3(256), 0, stream, args);

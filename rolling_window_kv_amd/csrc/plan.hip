@@ -1,160 +1,26 @@
-// Step plan: advance every stream's cache state by one clock step.
-//
-// REBASE  (Audio8 explainer, "Rolling KV Cache 三步拆解" steps 1-2): the ring
-//   holds the last W tokens; when full the oldest is pushed out and its slot
-//   reused.  The base b moves in multiples of the re-base chunk: b is the
-//   largest multiple not above the oldest retained position, and when it moves
-//   by D the retained K are rotated by R(-D) (rkv_roll_rebase).  The new token
-//   is written at relative position t - b.
-// COMPACT (voxtral.c explainer, section 二): rows grow to the capacity; when
-//   full, the newest W rows are kept (moved to row 0 by rkv_compact) and
-//   kv_pos_offset grows by the number dropped; the new row's rotary position
-//   is kv_pos_offset + its row.
-// ENC_CHUNK (same explainer, section 三): F frames per step into a ring of
-//   cap >= W + F slots at logical positions; frames attend back to
-//   max(origin, P - W).
-//
-// One block of 64 threads per stream.  All threads derive the integer plan
-// from the old state; thread 0 publishes plan and new state; thread i < d/2
-// fills the rotary tables of pair i (angles, cosines and sines in float64).
-
-#include <math.h>
+// Step plan kernel: advance every stream's cache state by one clock step
+// (the per-mode rules are in rkv_plan.h).  One wave of 64 threads per stream.
 
 #include "rkv_device.h"
 #include "rkv_internal.h"
+#include "rkv_plan.h"
 
 namespace rkv {
 namespace {
 
-struct PlanHead {
-  int64_t t, pos, pos_offset, first_pos, evict_pos;
-  int32_t slot, n_valid, delta, drop, evict_slot, new_rows;
-  rkv_stream_state next;
-};
-
-__device__ PlanHead make_plan(const rkv_stream_state& x, int mode, int dc, int F) {
-  PlanHead p;
-  p.next = x;
-  p.delta = 0;
-  p.drop = 0;
-  p.evict_pos = -1;
-  p.evict_slot = -1;
-  p.new_rows = 1;
-  if (mode == RKV_MODE_REBASE) {
-    const int64_t t = x.t + 1;
-    int32_t len = x.len;
-    if (len == x.window) {
-      p.evict_pos = t - x.window;
-      p.evict_slot = (int32_t)((t - x.origin) % x.window);
-    } else {
-      len += 1;
-    }
-    const int64_t oldest = t - len + 1;
-    const int64_t base = (int64_t)dc * (oldest / dc);
-    p.t = t;
-    p.slot = (int32_t)((t - x.origin) % x.window);
-    p.n_valid = len;
-    p.delta = (int32_t)(base - x.pos_offset);
-    p.pos = t - base;
-    p.pos_offset = base;
-    p.first_pos = oldest;
-    p.next.t = t;
-    p.next.len = len;
-    p.next.pos_offset = base;
-  } else if (mode == RKV_MODE_COMPACT) {
-    const int64_t t = x.t + 1;
-    int32_t len = x.len;
-    int64_t off = x.pos_offset;
-    if (len >= x.cap && len >= x.window) {
-      p.drop = len - x.window;
-      p.evict_pos = off;
-      off += p.drop;
-      len = x.window;
-    }
-    p.t = t;
-    p.slot = len;
-    len += 1;
-    p.n_valid = len;
-    p.pos = off + p.slot;
-    p.pos_offset = off;
-    p.first_pos = off;
-    p.next.t = t;
-    p.next.len = len;
-    p.next.pos_offset = off;
-  } else {  // RKV_MODE_ENC_CHUNK
-    const int64_t first = x.t + 1;
-    p.t = x.t + F;
-    p.slot = (int32_t)((first - x.origin) % x.cap);
-    const int32_t len = x.len + F < x.cap ? x.len + F : x.cap;
-    p.n_valid = len;
-    p.pos = first;
-    p.pos_offset = x.origin;
-    p.first_pos = first - x.window > x.origin ? first - x.window : x.origin;
-    p.new_rows = F;
-    p.next.t = p.t;
-    p.next.len = len;
-  }
-  return p;
-}
-
-struct Theta {
-  double v[RKV_MAX_HEAD_DIM / 2];
-};
-
 __global__ __launch_bounds__(64) void advance_kernel(rkv_stream_state* __restrict__ st,
                                                      rkv_step_plan* __restrict__ plan, int mode,
                                                      int dc, int F, int half, Theta th) {
-  const int s = blockIdx.x;
-  const int i = threadIdx.x;
-  const rkv_stream_state x = st[s];
-  const PlanHead p = make_plan(x, mode, dc, F);
-  __syncthreads();  // every thread has read the old state
-  rkv_step_plan* out = plan + s;
-  if (i == 0) {
-    st[s] = p.next;
-    out->t = p.t;
-    out->pos = p.pos;
-    out->pos_offset = p.pos_offset;
-    out->first_pos = p.first_pos;
-    out->evict_pos = p.evict_pos;
-    out->slot = p.slot;
-    out->n_valid = p.n_valid;
-    out->rebase_delta = p.delta;
-    out->compact_drop = p.drop;
-    out->evict_slot = p.evict_slot;
-    out->window = x.window;
-    out->cap = x.cap;
-    out->new_rows = p.new_rows;
-    for (int r = 0; r < 14; ++r) out->reserved[r] = 0;
-  }
-  // Only the rows and pairs a step uses are written (rows j < new_rows,
-  // pairs i < d/2); a zero delta has the exact table cos = 1, sin = 0.
-  if (i >= half) return;
-  const double theta = th.v[i];
-#pragma unroll 1
-  for (int j = 0; j < p.new_rows; ++j) {
-    double sn, cs;
-    sincos((double)(p.pos + j) * theta, &sn, &cs);
-    out->rope_new[j][0][i] = cs;
-    out->rope_new[j][1][i] = sn;
-  }
-  double sn = 0.0, cs = 1.0;
-  if (p.delta != 0) sincos((double)p.delta * theta, &sn, &cs);
-  out->rope_delta[0][i] = cs;
-  out->rope_delta[1][i] = sn;
+  advance_stream(st, plan, blockIdx.x, threadIdx.x, mode, dc, F, half, th);
 }
 
 }  // namespace
 
 hipError_t launch_advance(const rkv_cfg* cfg, rkv_stream_state* st, rkv_step_plan* plan,
                           hipStream_t stream) {
-  // theta_i = base^(-2i/d), i < d/2, computed once on the host in float64
-  Theta th;
-  const int half = cfg->head_dim / 2;
-  for (int i = 0; i < RKV_MAX_HEAD_DIM / 2; ++i)
-    th.v[i] = i < half ? pow(cfg->rope_base, -2.0 * (double)i / (double)cfg->head_dim) : 0.0;
   hipLaunchKernelGGL(advance_kernel, dim3(cfg->num_streams), dim3(64), 0, stream, st, plan,
-                     cfg->mode, cfg->rebase_chunk, cfg->new_rows, half, th);
+                     cfg->mode, cfg->rebase_chunk, cfg->new_rows, cfg->head_dim / 2,
+                     theta_table(cfg));
   return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "rkv.h"
+#include "rkv_plan.h"
 
 namespace rkv {
 
@@ -30,6 +31,12 @@ struct AttnArgs {
   int32_t nsplit;
   int32_t out_f32;
   float scale_log2;   // softmax scale * log2(e)
+  // Pipelined decode step: extra waves of the same launch compute the next
+  // step's plan into adv_plan and advance adv_state (null: none).
+  rkv_stream_state* adv_state;
+  rkv_step_plan* adv_plan;
+  int32_t adv_mode, adv_dc, adv_F, adv_half;
+  Theta adv_theta;
 };
 
 enum AttnKind { kDecodeRead = 0, kDecodeFused = 1, kEncoderFused = 2 };

@@ -38,6 +38,7 @@ ENTRY_POINTS = (
     "rkv_version", "rkv_strerror", "rkv_last_hip_error", "rkv_validate_cfg",
     "rkv_state_init_host", "rkv_state_init", "rkv_workspace_bytes", "rkv_advance", "rkv_append",
     "rkv_roll_rebase", "rkv_compact", "rkv_decode_attn", "rkv_decode_step",
+    "rkv_decode_step_pipelined",
     "rkv_encoder_chunk_attn",
 )
 
@@ -114,6 +115,8 @@ def lib():
             "rkv_compact": ([pc, vp, pk, vp], ctypes.c_int),
             "rkv_decode_attn": ([pc, vp, pk, vp, vp, vp, sz, vp], ctypes.c_int),
             "rkv_decode_step": ([pc, vp, pk, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "rkv_decode_step_pipelined": ([pc, vp, vp, vp, pk, vp, vp, vp, vp, vp, sz, vp],
+                                          ctypes.c_int),
             "rkv_encoder_chunk_attn": ([pc, vp, pk, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
@@ -267,6 +270,18 @@ def rkv_decode_step(cfg, plan, kv, q, k_new, v_new, out, workspace=None, stream=
                                                     _stream(stream)))
 
 
+def rkv_decode_step_pipelined(cfg, state, plan, plan_next, kv, q, k_new, v_new, out,
+                              workspace=None, stream=None):
+    """rkv_decode_step with `plan`, and the next step's plan into `plan_next`
+    (state advanced) in the same launch."""
+    wp, wb = _ws(workspace)
+    _check("rkv_decode_step_pipelined",
+           lib().rkv_decode_step_pipelined(ctypes.byref(cfg), _ptr(state), _ptr(plan),
+                                           _ptr(plan_next), ctypes.byref(kv), _ptr(q),
+                                           _ptr(k_new), _ptr(v_new), _ptr(out), wp, wb,
+                                           _stream(stream)))
+
+
 def rkv_encoder_chunk_attn(cfg, plan, kv, q, k_new, v_new, out, workspace=None, stream=None):
     wp, wb = _ws(workspace)
     _check("rkv_encoder_chunk_attn",
@@ -314,6 +329,8 @@ class Cache:
         with torch.cuda.device(self.state.device):
             rkv_state_init(cfg, self.state, window, cap, origin)
         self.plan = torch.zeros(S * PLAN_DTYPE.itemsize, dtype=torch.uint8, device=device)
+        # second plan buffer for rkv_decode_step_pipelined (plans alternate)
+        self.plan_next = torch.zeros_like(self.plan)
         nbytes = rkv_workspace_bytes(cfg, slots)
         self.workspace = (torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=device)
                           if nbytes else None)

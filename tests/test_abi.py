@@ -183,6 +183,18 @@ def test_calls_reject_bad_arguments_without_a_device(rkv):
                 N) == rkv.RKV_EALIGN
     assert call(rkv, "rkv_decode_step", c, F, ctypes.byref(kv), F, F, N, F, N, 0,
                 N) == rkv.RKV_EINVAL
+    # pipelined step: the plan read and the plan written must be distinct buffers
+    PL = ctypes.c_void_p(FAKE + 0x100000)
+    assert call(rkv, "rkv_decode_step_pipelined", c, F, F, F, ctypes.byref(kv), F, F, F, F, N,
+                0, N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_decode_step_pipelined", c, F, F, ctypes.c_void_p(FAKE + 64),
+                ctypes.byref(kv), F, F, F, F, N, 0, N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_decode_step_pipelined", c, N, F, PL, ctypes.byref(kv), F, F, F, F, N,
+                0, N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_decode_step_pipelined", c, F, F, ctypes.c_void_p(FAKE + 0x100008),
+                ctypes.byref(kv), F, F, F, F, N, 0, N) == rkv.RKV_EALIGN
+    assert call(rkv, "rkv_decode_step_pipelined", c, ctypes.c_void_p(FAKE + 4), F, PL,
+                ctypes.byref(kv), F, F, F, F, N, 0, N) == rkv.RKV_EALIGN
     # device state init: bad host arrays and mismatched streams fail before any copy
     W = np.full(cfg.num_streams, 375, np.int32)
     O = np.zeros(cfg.num_streams, np.int64)
