@@ -29,7 +29,7 @@
 // (v_perm) into the A operand (row c <-> dim CW*c + e for product e).  Output
 // lane (g4, c < 8) ends with dims [4*CW*g4, 4*CW*g4 + 4*CW) of column c.
 //
-// The rotated query is built once per workgroup (the waves split the rotary
+// The rotated query is built once per workgroup (all waves share the rotary
 // pairs) and shared through LDS.  Each wave requests its query chunks, rotary
 // tables and new row first and its first two tiles right after them (vector
 // loads complete in issue order), so set-up waits only for the small loads
@@ -40,7 +40,7 @@
 // The fused kinds also update the cache in the same launch, with results
 // identical to running rkv_roll_rebase, rkv_append and the read-only kind in
 // turn.  Decoder: during set-up the waves rotate the new K row from k_new in
-// float64 (one rotary chunk pair each), write K and V to the ring and leave
+// float64 (the rotary pairs split over all waves), write K and V to the ring and leave
 // both in LDS, from where the wave whose tile holds the new slot patches them
 // into its registers (its tile may have been read before the write).  In
 // REBASE mode, when the plan's delta D > 0, each wave re-bases the rows of its
@@ -203,40 +203,46 @@ void attn_kernel(AttnArgs a) {
   // Tiles read here are clamped into the allocation (rows past the valid
   // range are masked in process()).
   //
-  // Rotated query: wave w builds the rotary chunk pair (st, st + KH) with
-  // st = w, split into hi/lo bfloat16 columns, and shares it through LDS.
-  constexpr int QST = (KH + NW - 1) / NW;  // chunk pairs per wave
+  // Set-up work (rotated query, decoder's new K row) is split over all waves
+  // in units of one 32-bit word of one chunk pair: unit u covers elements
+  // 2w, 2w + 1 (w = u / KH) of chunks st and st + KH (st = u % KH) of the
+  // lane's 8-element slices; wave v takes units v, v + NW, ...
+  constexpr int UNITS = KH * 4;
+  constexpr int UPW = (UNITS + NW - 1) / NW;  // units per wave
   const bool qhas = col_q < a.G;
-  u32x4 qx1[QST], qx2[QST];
-  // cos/sin of this lane's rotary pairs at the new position (float64: the
+  uint32_t qw1[UPW], qw2[UPW];
+  // cos/sin of the unit's two rotary pairs at the new position (float64: the
   // decoder's new K row uses them as they are, the query in float32)
-  double rcs[QST][8], rsn[QST][8];
+  double rcs[UPW][2], rsn[UPW][2];
+  uint32_t kw1[UPW], kw2[UPW];
+  auto unit_st = [&](int k) { return (wave + NW * k) % KH; };
+  auto unit_w = [&](int k) { return ((wave + NW * k) / KH) & 3; };
   {
     const uint16_t* qp = a.q + vec_off(qhas ? col_q : 0);
     const int rrow = (KIND == kEncoderFused) ? col_q : 0;
 #pragma unroll
-    for (int k = 0; k < QST; ++k) {
-      const int st = wave + NW * k < KH ? wave + NW * k : KH - 1;
-      qx1[k] = qhas ? ld16(qp + 32 * st + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
-      qx2[k] = qhas ? ld16(qp + 32 * (st + KH) + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < UPW; ++k) {
+      const int st = unit_st(k), w = unit_w(k);
+      const int o = 32 * st + 8 * g4 + 2 * w;
+      qw1[k] = qhas ? *reinterpret_cast<const uint32_t*>(qp + o) : 0u;
+      qw2[k] = qhas ? *reinterpret_cast<const uint32_t*>(qp + o + 32 * KH) : 0u;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        rcs[k][e] = P->rope_new[rrow][0][32 * st + 8 * g4 + e];
-        rsn[k][e] = P->rope_new[rrow][1][32 * st + 8 * g4 + e];
+      for (int h = 0; h < 2; ++h) {
+        rcs[k][h] = P->rope_new[rrow][0][o + h];
+        rsn[k][h] = P->rope_new[rrow][1][o + h];
       }
     }
   }
-  // Decoder's new row: wave w rotates K chunk pair (st = w, st + KH); the last
-  // wave copies V.  Both are patched into their tile from LDS inside the loop.
-  u32x4 knew_c[QST][2];
+  // Decoder's new row: the last wave copies V.  K and V are patched into their
+  // tile from LDS inside the loop.
   VT vnew_c;
   if (KIND == kDecodeFused) {
     const uint16_t* kn = a.knew + new_off(0);
 #pragma unroll
-    for (int k = 0; k < QST; ++k) {
-      const int st = wave + NW * k < KH ? wave + NW * k : KH - 1;
-      knew_c[k][0] = ld16(kn + 32 * st + 8 * g4);
-      knew_c[k][1] = ld16(kn + 32 * (st + KH) + 8 * g4);
+    for (int k = 0; k < UPW; ++k) {
+      const int o = 32 * unit_st(k) + 8 * g4 + 2 * unit_w(k);
+      kw1[k] = *reinterpret_cast<const uint32_t*>(kn + o);
+      kw2[k] = *reinterpret_cast<const uint32_t*>(kn + o + 32 * KH);
     }
     vnew_c = VC::load(a.vnew + new_off(0) + CW * c);
   }
@@ -248,36 +254,25 @@ void attn_kernel(AttnArgs a) {
   load_tile(first, tb[0], kalloc - 1 > 0 ? kalloc - 1 : 0);
   load_tile(first + TK * NW, tb[1], kalloc - 1 > 0 ? kalloc - 1 : 0);
 
-  {
 #pragma unroll
-    for (int k = 0; k < QST; ++k) {
-      const int st = wave + NW * k;
-      if (st >= KH) continue;
-      u32x4 w1, w2;
+  for (int k = 0; k < UPW; ++k) {
+    if (wave + NW * k >= UNITS) continue;
+    const int st = unit_st(k), w = unit_w(k);
+    float y1[2], y2[2];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float y1[2], y2[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int e = 2 * w + h;
-          const float a1 = bf2f(elem8(qx1[k], e)), a2 = bf2f(elem8(qx2[k], e));
-          const float cq = (float)rcs[k][e], sq = (float)rsn[k][e];
-          y1[h] = fmaf(a1, cq, -(a2 * sq));
-          y2[h] = fmaf(a1, sq, a2 * cq);
-        }
-        const uint32_t h1 = cvt2_bf16(y1[0], y1[1]);
-        const uint32_t h2 = cvt2_bf16(y2[0], y2[1]);
-        if (part) {
-          w1[w] = cvt2_bf16(y1[0] - bf2f(h1 & 0xffffu), y1[1] - bf2f(h1 >> 16));
-          w2[w] = cvt2_bf16(y2[0] - bf2f(h2 & 0xffffu), y2[1] - bf2f(h2 >> 16));
-        } else {
-          w1[w] = h1;
-          w2[w] = h2;
-        }
-      }
-      sm_q[st][lane] = w1;
-      sm_q[st + KH][lane] = w2;
+    for (int h = 0; h < 2; ++h) {
+      const float a1 = bf2f((qw1[k] >> (16 * h)) & 0xffffu);
+      const float a2 = bf2f((qw2[k] >> (16 * h)) & 0xffffu);
+      const float cq = (float)rcs[k][h], sq = (float)rsn[k][h];
+      y1[h] = fmaf(a1, cq, -(a2 * sq));
+      y2[h] = fmaf(a1, sq, a2 * cq);
     }
+    const uint32_t h1 = cvt2_bf16(y1[0], y1[1]);
+    const uint32_t h2 = cvt2_bf16(y2[0], y2[1]);
+    reinterpret_cast<uint32_t*>(&sm_q[st][lane])[w] =
+        part ? cvt2_bf16(y1[0] - bf2f(h1 & 0xffffu), y1[1] - bf2f(h1 >> 16)) : h1;
+    reinterpret_cast<uint32_t*>(&sm_q[st + KH][lane])[w] =
+        part ? cvt2_bf16(y2[0] - bf2f(h2 & 0xffffu), y2[1] - bf2f(h2 >> 16)) : h2;
   }
 
   // ---- fused-update parameters ----
@@ -338,41 +333,31 @@ void attn_kernel(AttnArgs a) {
   };
 
   // Decoder RoPE-on-append: the waves rotate the new K row (float64,
-  // correctly rounded) chunk pair by chunk pair, write K and V to the ring and
-  // leave both in LDS for the wave whose tile holds the new slot.
+  // correctly rounded) unit by unit, write K and V to the ring and leave both
+  // in LDS for the wave whose tile holds the new slot.
   if (KIND == kDecodeFused) {
 #pragma unroll
-    for (int k = 0; k < QST; ++k) {
-      const int st = wave + NW * k;
-      if (st >= KH) continue;
-      u32x4 w1, w2, r1, r2;
+    for (int k = 0; k < UPW; ++k) {
+      if (wave + NW * k >= UNITS) continue;
+      const int st = unit_st(k), w = unit_w(k);
+      double y1[2], y2[2];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        double y1[2], y2[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int e = 2 * w + h;
-          const int i = 32 * st + 8 * g4 + e;
-          rotate_pair64(bf2f(elem8(knew_c[k][0], e)), bf2f(elem8(knew_c[k][1], e)), rcs[k][e],
-                        rsn[k][e], y1[h], y2[h]);
-        }
-        w1[w] = cvt2_bf16_f64(y1[0], y1[1]);
-        w2[w] = cvt2_bf16_f64(y2[0], y2[1]);
-        if (COMP) {
-          r1[w] = cvt2_bf16_f64(y1[0] - (double)bf2f(w1[w] & 0xffffu),
-                                y1[1] - (double)bf2f(w1[w] >> 16));
-          r2[w] = cvt2_bf16_f64(y2[0] - (double)bf2f(w2[w] & 0xffffu),
-                                y2[1] - (double)bf2f(w2[w] >> 16));
-        }
-      }
+      for (int h = 0; h < 2; ++h)
+        rotate_pair64(bf2f((kw1[k] >> (16 * h)) & 0xffffu), bf2f((kw2[k] >> (16 * h)) & 0xffffu),
+                      rcs[k][h], rsn[k][h], y1[h], y2[h]);
+      const uint32_t w1 = cvt2_bf16_f64(y1[0], y1[1]);
+      const uint32_t w2 = cvt2_bf16_f64(y2[0], y2[1]);
       if (c == 0) {
-        sm_newk[st][g4] = w1;
-        sm_newk[st + KH][g4] = w2;
-        st16(Kp + slot_new * rs + 32 * st + 8 * g4, w1);
-        st16(Kp + slot_new * rs + 32 * (st + KH) + 8 * g4, w2);
+        const int o = 32 * st + 8 * g4 + 2 * w;
+        reinterpret_cast<uint32_t*>(&sm_newk[st][g4])[w] = w1;
+        reinterpret_cast<uint32_t*>(&sm_newk[st + KH][g4])[w] = w2;
+        *reinterpret_cast<uint32_t*>(Kp + slot_new * rs + o) = w1;
+        *reinterpret_cast<uint32_t*>(Kp + slot_new * rs + o + 32 * KH) = w2;
         if (COMP) {
-          st16(Lp + slot_new * rs + 32 * st + 8 * g4, r1);
-          st16(Lp + slot_new * rs + 32 * (st + KH) + 8 * g4, r2);
+          *reinterpret_cast<uint32_t*>(Lp + slot_new * rs + o) =
+              cvt2_bf16_f64(y1[0] - (double)bf2f(w1 & 0xffffu), y1[1] - (double)bf2f(w1 >> 16));
+          *reinterpret_cast<uint32_t*>(Lp + slot_new * rs + o + 32 * KH) =
+              cvt2_bf16_f64(y2[0] - (double)bf2f(w2 & 0xffffu), y2[1] - (double)bf2f(w2 >> 16));
         }
       }
     }
