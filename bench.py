@@ -452,7 +452,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": c["name"], "layers": L, "streams": S,
-                   "path": args.path, "alg_bytes_per_stream_layer_step": b_sl},
+                   "path": args.path if c["mode"] != "enc" else "fused",
+                   "alg_bytes_per_stream_layer_step": b_sl},
         "achieved_GBps_step": round(step_gbps, 1),
         "hbm_frac_step": round(step_gbps / PEAK_HBM_GBPS, 4),
         "clock_steps_per_s": round(K / secs, 1),
