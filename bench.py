@@ -3,14 +3,17 @@
 Default workload: 36 layers x 64 streams, 16 query / 2 KV heads, head_dim 128,
 bf16 rings of W = 375 positions (30 s at the 80 ms clock), base re-based in
 chunks of 25 positions.  A step is one clock step of every stream through the
-whole path: rkv_advance (plan) + rkv_decode_step (re-base, append and GQA
-decode attention for all 36 layers in one pass).  Inputs are synthetic
-N(0, 1) bf16 tensors already resident on the GPU (a pool of steps cycled).
+whole path: the step plan, re-base, append and GQA decode attention for all
+36 layers -- by default one rkv_decode_step_pipelined launch, which also
+computes the next step's plan (--path fused: rkv_advance + rkv_decode_step;
+--path separate: the individual calls).  Inputs are synthetic N(0, 1) bf16
+tensors already resident on the GPU (a pool of steps cycled).
 
 Prints one JSON line: stream-layer decode steps per second (value), the
 roofline of the dominant kernel (algorithmic bytes per launch over the
-launch's average duration, timed with HIP events on the launch stream), and
-the CPU oracle timed on a bounded sample on the host cores.
+launch's average duration, timed with HIP events on the launch stream on a
+sample of the timed launches), and the CPU oracle timed on a bounded sample
+on the host cores.
 
 Other workloads (--config): 1 = one layer x one stream, re-base every step
 (compensated); 3 = 256 streams of mixed windows 375/250/188 with start
@@ -306,24 +309,48 @@ def run_gpu(c, args):
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
+    # Live kernel timing inside the timed region, sampled so that the event
+    # records barely touch the step rate (a pair around every launch costs
+    # several microseconds per step).  Pipelined decoder steps are one launch
+    # of the attention kernel each: a pair brackets RUN consecutive launches
+    # (every GAP-th run) and the mean launch duration is its time / RUN.
+    # Otherwise other kernels run between attention launches: a pair around
+    # the attention launch of every RUN-th step.
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    RUN, GAP = 8, 4
+    bracket = pipelined and c["mode"] == "rebase" and K >= RUN
+    ev_runs, ev_steps = {}, {}
+    if args.kernel_events:
+        for n in (range(0, K - RUN + 1, RUN * GAP) if bracket else range(0, K, RUN)):
+            pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            (ev_runs if bracket else ev_steps)[n] = pair
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for n in range(K):
-        step(i, evs[n] if args.kernel_events else None)
+        if n in ev_runs:
+            ev_runs[n][0].record(stream)
+        step(i, ev_steps.get(n))
+        if n - RUN + 1 in ev_runs:
+            ev_runs[n - RUN + 1][1].record(stream)
         i += 1
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     elapsed_ms = start.elapsed_time(end)
-    kernel_ms = (float(np.mean([a.elapsed_time(b) for a, b in evs]))
-                 if args.kernel_events else None)
+    kernel_ms, kernel_samples = None, 0
+    if ev_runs:
+        kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_runs.values()])) / RUN
+        kernel_samples = RUN * len(ev_runs)
+    elif ev_steps:
+        kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_steps.values()]))
+        kernel_samples = len(ev_steps)
     return dict(cfg=cfg, elapsed_ms=elapsed_ms, kernel_ms=kernel_ms, wall_s=wall,
+                kernel_samples=kernel_samples,
+                kernel_timing="event pair per run of %d back-to-back launches" % RUN
+                if ev_runs else "event pair around sampled launches",
                 setup_s=setup_s, prefill=prefill)
 
 
@@ -437,6 +464,8 @@ def main():
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                     "traffic": traffic, "kernel": kernel,
                     "kernel_ms": round(r["kernel_ms"], 5),
+                    "kernel_launches_timed": r["kernel_samples"],
+                    "kernel_timing": r["kernel_timing"],
                     "alg_bytes_per_launch": per_launch}
     res = {
         "metric": METRIC,
