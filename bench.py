@@ -354,10 +354,12 @@ def run_gpu(c, args):
                 setup_s=setup_s, prefill=prefill)
 
 
-def summarize_rocprof(root):
+def summarize_rocprof(root, last=0):
     """Per-kernel figures from a rocprofv3 CSV output folder: its own --stats
-    table, mean dispatch duration from the kernel trace, and mean counter
-    values per dispatch (FETCH_SIZE / WRITE_SIZE are in KiB)."""
+    table, mean dispatch duration from the kernel trace (and, with last > 0,
+    the mean of each kernel's last `last` dispatches, e.g. a bench run's
+    warm-up and timed steps without its set-up), and mean counter values per
+    dispatch (FETCH_SIZE / WRITE_SIZE are in KiB)."""
     import csv
     import glob
     from collections import OrderedDict, defaultdict
@@ -378,9 +380,11 @@ def summarize_rocprof(root):
         for r in csv.DictReader(open(path)):
             dur[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
         lines.append(f"# kernel trace: {os.path.relpath(path, root)}")
-        lines.append(f"{'calls':>7} {'mean_us':>10} {'median_us':>10}  kernel")
+        tail = f" {'last%d_mean_us' % last:>15}" if last else ""
+        lines.append(f"{'calls':>7} {'mean_us':>10} {'median_us':>10}{tail}  kernel")
         for name, d in sorted(dur.items(), key=lambda x: -sum(x[1])):
-            lines.append(f"{len(d):7d} {np.mean(d) / 1e3:10.2f} {np.median(d) / 1e3:10.2f}  "
+            lt = f" {np.mean(d[-last:]) / 1e3:15.2f}" if last else ""
+            lines.append(f"{len(d):7d} {np.mean(d) / 1e3:10.2f} {np.median(d) / 1e3:10.2f}{lt}  "
                          f"{short(name)}")
     for path in sorted(glob.glob(os.path.join(root, "**", "*_counter_collection.csv"),
                             recursive=True)):
@@ -421,9 +425,12 @@ def main():
                          "the known-size kernel that scales the HBM byte counters")
     ap.add_argument("--summarize-rocprof", metavar="DIR", default=None,
                     help="print per-kernel figures from a rocprofv3 CSV output folder and exit")
+    ap.add_argument("--summarize-last", type=int, default=0, metavar="N",
+                    help="with --summarize-rocprof: also the mean of each kernel's last N "
+                         "dispatches")
     args = ap.parse_args()
     if args.summarize_rocprof:
-        print(summarize_rocprof(args.summarize_rocprof))
+        print(summarize_rocprof(args.summarize_rocprof, args.summarize_last))
         return
     if args.copy_calibration:
         import torch
