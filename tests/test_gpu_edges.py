@@ -1,0 +1,66 @@
+"""Degenerate and boundary cases of the decoder path against the float64
+oracle and closed forms: a one-slot window (the output is the newest V), MHA
+with one query per KV head at head_dim 64, eight query heads on one KV head,
+and a zero query (the output is the mean of V over the window)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as att
+from rolling_window_kv_amd import synth
+
+from gpu_util import check_close, device, f64, rkv_mod, run_decoder, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_one_slot_window_returns_newest_value(fused):
+    rkv = rkv_mod()
+    dev = device()
+    L, S, T, hq, hkv, d = 2, 3, 9, 16, 2, 128
+    say(f"case: W=1 fused={fused}")
+    q, k, v = synth.decoder_pool(31, L, S, T, hq, hkv, d)
+    cfg = rkv.make_cfg(S, L, rebase_chunk=1)
+    _, out, _ = run_decoder(rkv, cfg, 1, 1, 1, np.array([0, 4, 9], np.int64), q.to(dev), k.to(dev),
+                            v.to(dev), fused)
+    got = f64(out)                                          # [T, L, S, Hq, d]
+    want = np.repeat(f64(v), hq // hkv, axis=3)             # query head h reads KV head h // G
+    check_close(got, want, 0.0, "W=1 output == newest V")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 64), (8, 1, 128)])
+def test_head_layouts_against_oracle(hq, hkv, d):
+    rkv = rkv_mod()
+    dev = device()
+    L, S, T, W, dc = 2, 3, 70, 33, 4
+    say(f"case: Hq={hq} Hkv={hkv} d={d} W={W} dc={dc}")
+    q, k, v = synth.decoder_pool(32, L, S, T, hq, hkv, d)
+    cfg = rkv.make_cfg(S, L, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, rebase_chunk=dc)
+    _, out, _ = run_decoder(rkv, cfg, W, W, W, 0, q.to(dev), k.to(dev), v.to(dev), True)
+    got = f64(out)
+    for l in range(L):
+        for s in range(S):
+            qh, kh, vh = (f64(x)[:, l, s] for x in (q, k, v))
+            exact = att.window_decode(qh, kh, vh, W, 1e6)
+            want = np.stack([exact[t] for t in range(T)])
+            check_close(got[:, l, s], want, 2e-2, f"Hq={hq} Hkv={hkv} d={d} l{l} s{s}")
+
+
+def test_zero_query_gives_window_mean_of_values():
+    rkv = rkv_mod()
+    dev = device()
+    L, S, T, W, hq, hkv, d = 1, 2, 60, 21, 16, 2, 128
+    say("case: q = 0")
+    _, k, v = synth.decoder_pool(33, L, S, T, hq, hkv, d)
+    q = torch.zeros((T, L, S, hq, d), dtype=torch.bfloat16)
+    cfg = rkv.make_cfg(S, L, rebase_chunk=5, flags=rkv.RKV_F_OUT_F32)
+    _, out, _ = run_decoder(rkv, cfg, W, W, W, 0, q.to(dev), k.to(dev), v.to(dev), True,
+                            out_dtype=torch.float32)
+    got = f64(out)
+    vv = f64(v)
+    for t in (0, 5, W - 1, W, T - 1):
+        lo = max(0, t - W + 1)
+        mean = vv[lo:t + 1].mean(axis=0)                   # [L, S, Hkv, d]
+        want = np.repeat(mean, hq // hkv, axis=2)
+        check_close(got[t], want, 1e-5, f"q=0 step {t}: mean of V over the window")
