@@ -102,43 +102,44 @@ __global__ __launch_bounds__(256) void rebase_kernel(const rkv_step_plan* __rest
 
 // ---------------------------------------------------------------------------
 // Compaction move (voxtral.c explainer, section 二): rows [drop, drop + W) go
-// to [0, W) in row order.  The ranges overlap, so one wave moves a column
-// group of every row front to back in batches of at most `drop` rows: each
-// batch reads rows that no earlier batch wrote and writes rows whose reads
-// have completed, which makes the in-place forward move safe.  Column groups
-// (and K versus V) are independent, giving the parallelism.
+// to [0, W) in row order.  The ranges overlap, so the rows are moved front to
+// back in batches of at most `drop` rows: a batch reads rows that no earlier
+// batch wrote and writes rows that only earlier batches read.  One block moves
+// the K (or V) rows of one item, whole rows at a time; the barrier after each
+// batch's stores (which need its loads' data) makes every read of the batch
+// complete before the next batch writes.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(64) void compact_kernel(const rkv_step_plan* __restrict__ plan,
-                                                     RingArgs ring, int S, int H) {
-  constexpr int CG = 4;                 // column groups per row
-  constexpr int LPR = D / (8 * CG);     // lanes per row (16 bytes each)
-  constexpr int RPI = 64 / LPR;         // rows per load instruction
-  constexpr int NB = 4;                 // loads in flight per lane
+__global__ __launch_bounds__(256) void compact_kernel(const rkv_step_plan* __restrict__ plan,
+                                                      RingArgs ring, int S, int H) {
+  constexpr int TPR = D / 8;            // threads per row (16 bytes each)
+  constexpr int RPR = 256 / TPR;        // rows per load instruction of the block
+  constexpr int NB = 8;                 // loads in flight per thread
   int l, s, g;
   item_coords(blockIdx.x, H, S, l, s, g);
   const rkv_step_plan* P = plan + s;
   const int drop = P->compact_drop;
   if (drop == 0 || P->cap > ring.slots) return;
   const int rows = P->window;
-  uint16_t* base = (blockIdx.z == 0 ? ring.k : ring.v) + (int64_t)l * ring.ls +
+  uint16_t* base = (blockIdx.y == 0 ? ring.k : ring.v) + (int64_t)l * ring.ls +
                    (int64_t)s * ring.ss + (int64_t)g * ring.hs;
-  const int lane = threadIdx.x;
-  const int col = blockIdx.y * (D / CG) + (lane % LPR) * 8;
-  const int ro = lane / LPR;
-  const int batch = RPI * NB < drop ? RPI * NB : drop;
+  const int col = (threadIdx.x % TPR) * 8;
+  const int ro = threadIdx.x / TPR;
+  const int batch = RPR * NB < drop ? RPR * NB : drop;
   for (int r0 = 0; r0 < rows; r0 += batch) {
+    const int rend = r0 + batch < rows ? r0 + batch : rows;
     u32x4 buf[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const int r = r0 + ro + RPI * k;
-      if (r < r0 + batch && r < rows) buf[k] = ld16(base + (int64_t)(r + drop) * ring.rs + col);
+      const int r = r0 + ro + RPR * k;
+      if (r < rend) buf[k] = ld16(base + (int64_t)(r + drop) * ring.rs + col);
     }
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const int r = r0 + ro + RPI * k;
-      if (r < r0 + batch && r < rows) st16(base + (int64_t)r * ring.rs + col, buf[k]);
+      const int r = r0 + ro + RPR * k;
+      if (r < rend) st16(base + (int64_t)r * ring.rs + col, buf[k]);
     }
+    __syncthreads();
   }
 }
 
@@ -185,11 +186,11 @@ hipError_t launch_rebase(const rkv_cfg* cfg, const rkv_step_plan* plan, const Ri
 hipError_t launch_compact(const rkv_cfg* cfg, const rkv_step_plan* plan, const RingArgs& ring,
                           hipStream_t stream) {
   const int S = cfg->num_streams, H = cfg->num_kv_heads, L = cfg->num_layers;
-  const dim3 grid(L * S * H, 4, 2);
+  const dim3 grid(L * S * H, 2);
   if (cfg->head_dim == 128)
-    hipLaunchKernelGGL((compact_kernel<128>), grid, dim3(64), 0, stream, plan, ring, S, H);
+    hipLaunchKernelGGL((compact_kernel<128>), grid, dim3(256), 0, stream, plan, ring, S, H);
   else
-    hipLaunchKernelGGL((compact_kernel<64>), grid, dim3(64), 0, stream, plan, ring, S, H);
+    hipLaunchKernelGGL((compact_kernel<64>), grid, dim3(256), 0, stream, plan, ring, S, H);
   return hipGetLastError();
 }
 
