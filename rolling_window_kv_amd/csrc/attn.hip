@@ -74,19 +74,21 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// A lane's V chunk of one row (CW elements; 16 lanes cover a row, so each
+// load instruction reads whole lines: V rows are streamed, read once a launch).
 template <int CW>
 struct VChunk;
 template <>
 struct VChunk<8> {
   typedef u32x4 T;
-  static __device__ __forceinline__ T load(const uint16_t* p) { return ld16(p); }
+  static __device__ __forceinline__ T load(const uint16_t* p) { return ld16_stream(p); }
   static __device__ __forceinline__ void store(uint16_t* p, const T& w) { st16(p, w); }
   static __device__ __forceinline__ T zero() { return u32x4{0u, 0u, 0u, 0u}; }
 };
 template <>
 struct VChunk<4> {
   typedef u32x2 T;
-  static __device__ __forceinline__ T load(const uint16_t* p) { return ld8(p); }
+  static __device__ __forceinline__ T load(const uint16_t* p) { return ld8_stream(p); }
   static __device__ __forceinline__ void store(uint16_t* p, const T& w) { st8(p, w); }
   static __device__ __forceinline__ T zero() { return u32x2{0u, 0u}; }
 };
