@@ -270,6 +270,78 @@ int rkv_encoder_chunk_attn(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
                            void* workspace, size_t workspace_bytes,
                            void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Continuous mode (voxtral.c explainer, section 四).  In live transcription
+ * the decoder is restarted hard -- its context is dropped -- when the model
+ * ends an utterance (EOS), when its cache would grow past
+ * STREAM_MAX_DECODE_KV positions (bounding the attention cost), on a run of
+ * control tokens, and when audio advances while it produces nothing; the
+ * encoder cache (a separate state) and the streaming pipeline keep running.
+ * rkv_restart_step decides on the host; rkv_reset_streams restarts caches.
+ * ------------------------------------------------------------------------- */
+
+/* Restart the decoder caches of the listed streams: stream h_streams[i]
+ * starts again at position h_origin[i] exactly as rkv_state_init starts a
+ * stream (same window and capacity, no valid rows); its ring rows stay in
+ * memory but are no longer attended.  Other streams are untouched.
+ * d_plan: NULL when the next call for these states is rkv_advance.  A
+ * pipelined loop has already written the next step's plan: pass that plan,
+ * and the listed streams are also advanced by that step and their entries of
+ * d_plan rewritten, as if the restart had come before the launch that wrote
+ * it.  The lists (host memory) are applied in order, so a stream listed twice
+ * ends at its last origin; n = 0 does nothing.  Asynchronous on hip_stream
+ * and allocation-free: the lists travel in kernel arguments (up to 64 streams
+ * per launch) and the arrays may be reused as soon as the call returns.
+ * Errors: RKV_EINVAL (null pointer with n > 0, n < 0, a stream index outside
+ * [0, S)), RKV_ESTATE (an origin < 0), RKV_EALIGN (d_state not 8-byte or
+ * d_plan not 16-byte aligned). */
+int rkv_reset_streams(const rkv_cfg* cfg, rkv_stream_state* d_state, rkv_step_plan* d_plan,
+                      int32_t n, const int32_t* h_streams, const int64_t* h_origin,
+                      void* hip_stream);
+
+#define RKV_STREAM_MAX_DECODE_KV 2000   /* the page's STREAM_MAX_DECODE_KV */
+
+enum {
+  RKV_RESTART_NONE = 0,
+  RKV_RESTART_EOS = 1,
+  RKV_RESTART_KV_OVERFLOW = 2,
+  RKV_RESTART_NONTEXT_RUN = 3,
+  RKV_RESTART_STALL = 4
+};
+
+/* Restart policy (host memory).  A step's token is text (id >=
+ * text_token_min), a control token (0 <= id < text_token_min), or none
+ * (id < 0).  Thresholds <= 0 (eos_token < 0) switch a condition off. */
+typedef struct rkv_restart_cfg {
+  int64_t max_decode_kv;   /* restart after the step that brings the decoder to
+                              this many positions since its last restart, so no
+                              step attends over more (RKV_STREAM_MAX_DECODE_KV) */
+  int32_t eos_token;       /* restart after this token */
+  int32_t text_token_min;  /* >= 0 */
+  int32_t nontext_run;     /* restart after this many consecutive control tokens */
+  int32_t stall_steps;     /* restart after this many consecutive steps without a token */
+} rkv_restart_cfg;
+
+/* Per-stream policy counters (host memory, all zero for a fresh stream). */
+typedef struct rkv_restart_state {
+  int64_t decode_len;  /* positions decoded since the last restart */
+  int64_t restarts;    /* restarts so far */
+  int32_t nontext;     /* current run of control tokens */
+  int32_t idle;        /* current run of steps without a token */
+} rkv_restart_state;
+
+/* One clock step of the restart policy for num_streams streams: h_token[s]
+ * is the token the decoder emitted for stream s at this step.  Updates
+ * h_state[s]; writes h_reason[s] (RKV_RESTART_*; the first condition that
+ * holds, in the page's order EOS, overflow, control-token run, stall) and the
+ * indices of the streams to restart, increasing, to h_restart[0..count) (each
+ * output may be NULL).  Returns count (>= 0), or RKV_EINVAL (null cfg, state
+ * or token array, num_streams < 1, text_token_min < 0).  A restarted stream's
+ * counters start over.  Host only: no device, no HIP call. */
+int rkv_restart_step(const rkv_restart_cfg* cfg, rkv_restart_state* h_state,
+                     int32_t num_streams, const int32_t* h_token, int32_t* h_reason,
+                     int32_t* h_restart);
+
 #ifdef __cplusplus
 }
 #endif

@@ -191,18 +191,9 @@ int rkv_state_init_host(const rkv_cfg* cfg, const int32_t* h_window, const int32
         break;
     }
   }
-  for (int s = 0; s < cfg->num_streams; ++s) {
-    rkv_stream_state& st = h_state[s];
-    memset(&st, 0, sizeof(st));
-    st.t = h_origin[s] - 1;
-    st.origin = h_origin[s];
-    st.pos_offset = cfg->mode == RKV_MODE_REBASE
-                        ? (int64_t)cfg->rebase_chunk * (h_origin[s] / cfg->rebase_chunk)
-                        : h_origin[s];
-    st.len = 0;
-    st.window = h_window[s];
-    st.cap = h_cap[s];
-  }
+  for (int s = 0; s < cfg->num_streams; ++s)
+    h_state[s] = rkv::initial_state(h_origin[s], h_window[s], h_cap[s], cfg->mode,
+                                    cfg->rebase_chunk);
   return RKV_OK;
 }
 
@@ -226,6 +217,42 @@ int rkv_state_init(const rkv_cfg* cfg, rkv_stream_state* d_state, const int32_t*
                                   hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_status(e);
+  }
+  return RKV_OK;
+}
+
+int rkv_reset_streams(const rkv_cfg* cfg, rkv_stream_state* d_state, rkv_step_plan* d_plan,
+                      int32_t n, const int32_t* h_streams, const int64_t* h_origin,
+                      void* hip_stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!d_state || n < 0) return RKV_EINVAL;
+  if (n > 0 && (!h_streams || !h_origin)) return RKV_EINVAL;
+  if ((uintptr_t)d_state & 7u) return RKV_EALIGN;
+  if (d_plan && !aligned16(d_plan)) return RKV_EALIGN;
+  for (int32_t i = 0; i < n; ++i) {
+    if (h_streams[i] < 0 || h_streams[i] >= cfg->num_streams) return RKV_EINVAL;
+    if (h_origin[i] < 0) return RKV_ESTATE;
+  }
+  // Launches of at most ResetList::kMax streams, in list order; a launch ends
+  // before a stream already in it, so each launch resets distinct streams and
+  // a repeated stream takes its later origin.
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  rkv::ResetList list;
+  list.n = 0;
+  for (int32_t i = 0; i <= n; ++i) {
+    bool flush = i == n || list.n == rkv::ResetList::kMax;
+    for (int j = 0; !flush && j < list.n; ++j) flush = list.stream[j] == h_streams[i];
+    if (flush && list.n > 0) {
+      hipError_t e = rkv::launch_reset(cfg, d_state, d_plan, list, stream);
+      if (e != hipSuccess) return hip_status(e);
+      list.n = 0;
+    }
+    if (i < n) {
+      list.stream[list.n] = h_streams[i];
+      list.origin[list.n] = h_origin[i];
+      ++list.n;
+    }
   }
   return RKV_OK;
 }

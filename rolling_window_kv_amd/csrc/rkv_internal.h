@@ -48,6 +48,16 @@ __host__ __device__ inline int64_t partial_floats(int d) { return 16 + 8 * (int6
 
 hipError_t launch_advance(const rkv_cfg* cfg, rkv_stream_state* st, rkv_step_plan* plan,
                           hipStream_t stream);
+
+// Streams restarted by one reset launch (passed by value in kernel arguments).
+struct ResetList {
+  static constexpr int kMax = 64;
+  int32_t n;
+  int32_t stream[kMax];
+  int64_t origin[kMax];
+};
+hipError_t launch_reset(const rkv_cfg* cfg, rkv_stream_state* st, rkv_step_plan* plan,
+                        const ResetList& list, hipStream_t stream);
 hipError_t launch_append(const rkv_cfg* cfg, const rkv_step_plan* plan, const RingArgs& ring,
                          const uint16_t* knew, const uint16_t* vnew, hipStream_t stream);
 hipError_t launch_rebase(const rkv_cfg* cfg, const rkv_step_plan* plan, const RingArgs& ring,

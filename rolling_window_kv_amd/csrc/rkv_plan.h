@@ -35,6 +35,21 @@ struct PlanHead {
   rkv_stream_state next;
 };
 
+// State before the first step of a stream whose first position is `origin`
+// (window and capacity already validated for the mode).
+__host__ __device__ inline rkv_stream_state initial_state(int64_t origin, int32_t window,
+                                                          int32_t cap, int mode, int dc) {
+  rkv_stream_state st;
+  st.t = origin - 1;
+  st.origin = origin;
+  st.pos_offset = mode == RKV_MODE_REBASE ? (int64_t)dc * (origin / dc) : origin;
+  st.len = 0;
+  st.window = window;
+  st.cap = cap;
+  st.reserved[0] = st.reserved[1] = st.reserved[2] = 0;
+  return st;
+}
+
 __device__ inline PlanHead make_plan(const rkv_stream_state& x, int mode, int dc, int F) {
   PlanHead p;
   p.next = x;
@@ -100,16 +115,14 @@ __device__ inline PlanHead make_plan(const rkv_stream_state& x, int mode, int dc
   return p;
 }
 
-// Advance stream s by one step with the 64 lanes of one wave (lane = 0..63):
-// every lane derives the plan from the old state (the loads of one wave
-// complete before any of its later stores, so lane 0 may then overwrite the
-// state); lane 0 publishes the plan header and the new state; lane i < d/2
-// fills the rotary tables of pair i, only for the rows and pairs a step uses
-// (rows j < new_rows; a zero delta has the exact table cos = 1, sin = 0).
-__device__ inline void advance_stream(rkv_stream_state* __restrict__ st,
-                                      rkv_step_plan* __restrict__ plan, int s, int lane, int mode,
-                                      int dc, int F, int half, const Theta& th) {
-  const rkv_stream_state x = st[s];
+// Advance stream s by one step from state x with the 64 lanes of one wave
+// (lane = 0..63; every lane holds x): lane 0 publishes the plan header and the
+// new state; lane i < d/2 fills the rotary tables of pair i, only for the
+// rows and pairs a step uses (rows j < new_rows; a zero delta has the exact
+// table cos = 1, sin = 0).
+__device__ inline void advance_from(const rkv_stream_state& x, rkv_stream_state* __restrict__ st,
+                                    rkv_step_plan* __restrict__ plan, int s, int lane, int mode,
+                                    int dc, int F, int half, const Theta& th) {
   const PlanHead p = make_plan(x, mode, dc, F);
   rkv_step_plan* out = plan + s;
   if (lane == 0) {
@@ -142,6 +155,16 @@ __device__ inline void advance_stream(rkv_stream_state* __restrict__ st,
   if (p.delta != 0) sincos((double)p.delta * theta, &sn, &cs);
   out->rope_delta[0][lane] = cs;
   out->rope_delta[1][lane] = sn;
+}
+
+// Advance stream s by one step from its stored state: every lane reads the
+// old state first (the loads of one wave complete before any of its later
+// stores, so lane 0 may then overwrite it).
+__device__ inline void advance_stream(rkv_stream_state* __restrict__ st,
+                                      rkv_step_plan* __restrict__ plan, int s, int lane, int mode,
+                                      int dc, int F, int half, const Theta& th) {
+  const rkv_stream_state x = st[s];
+  advance_from(x, st, plan, s, lane, mode, dc, F, half, th);
 }
 
 // Host: the theta table of a configuration.

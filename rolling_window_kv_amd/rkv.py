@@ -39,8 +39,15 @@ ENTRY_POINTS = (
     "rkv_state_init_host", "rkv_state_init", "rkv_workspace_bytes", "rkv_advance", "rkv_append",
     "rkv_roll_rebase", "rkv_compact", "rkv_decode_attn", "rkv_decode_step",
     "rkv_decode_step_pipelined",
-    "rkv_encoder_chunk_attn",
+    "rkv_encoder_chunk_attn", "rkv_reset_streams", "rkv_restart_step",
 )
+
+RKV_STREAM_MAX_DECODE_KV = 2000
+RKV_RESTART_NONE = 0
+RKV_RESTART_EOS = 1
+RKV_RESTART_KV_OVERFLOW = 2
+RKV_RESTART_NONTEXT_RUN = 3
+RKV_RESTART_STALL = 4
 
 
 class RkvError(RuntimeError):
@@ -72,6 +79,18 @@ class rkv_kv_view(ctypes.Structure):
         ("slots", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
+
+class rkv_restart_cfg(ctypes.Structure):
+    _fields_ = [
+        ("max_decode_kv", ctypes.c_int64), ("eos_token", ctypes.c_int32),
+        ("text_token_min", ctypes.c_int32), ("nontext_run", ctypes.c_int32),
+        ("stall_steps", ctypes.c_int32),
+    ]
+
+
+RESTART_STATE_DTYPE = np.dtype([
+    ("decode_len", "<i8"), ("restarts", "<i8"), ("nontext", "<i4"), ("idle", "<i4"),
+])
 
 STATE_DTYPE = np.dtype([
     ("t", "<i8"), ("origin", "<i8"), ("pos_offset", "<i8"),
@@ -118,6 +137,9 @@ def lib():
             "rkv_decode_step_pipelined": ([pc, vp, vp, vp, pk, vp, vp, vp, vp, vp, sz, vp],
                                           ctypes.c_int),
             "rkv_encoder_chunk_attn": ([pc, vp, pk, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "rkv_reset_streams": ([pc, vp, vp, i32, vp, vp, vp], ctypes.c_int),
+            "rkv_restart_step": ([ctypes.POINTER(rkv_restart_cfg), vp, i32, vp, vp, vp],
+                                 ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -223,6 +245,40 @@ def rkv_state_init_host(cfg, window, cap, origin) -> np.ndarray:
                                    o.ctypes.data, out.ctypes.data)
     _check("rkv_state_init_host", rc)
     return out
+
+
+def rkv_reset_streams(cfg, state, plan, streams, origin, stream=None):
+    """Restart the decoder caches of `streams` at positions `origin` (host
+    sequences); `plan`: None, or the already written plan of the coming step
+    (pipelined loops), whose entries for these streams are rewritten."""
+    st = np.ascontiguousarray(np.asarray(streams, dtype=np.int32).reshape(-1))
+    org = np.ascontiguousarray(np.broadcast_to(np.asarray(origin, dtype=np.int64), st.shape))
+    _check("rkv_reset_streams",
+           lib().rkv_reset_streams(ctypes.byref(cfg), _ptr(state), _ptr(plan), int(st.size),
+                                   st.ctypes.data if st.size else None,
+                                   org.ctypes.data if st.size else None, _stream(stream)))
+
+
+def make_restart_cfg(max_decode_kv=RKV_STREAM_MAX_DECODE_KV, eos_token=-1, text_token_min=0,
+                     nontext_run=0, stall_steps=0) -> rkv_restart_cfg:
+    return rkv_restart_cfg(max_decode_kv, eos_token, text_token_min, nontext_run, stall_steps)
+
+
+def rkv_restart_step(cfg, state, tokens):
+    """One clock step of the continuous-mode restart policy (host only).
+    state: RESTART_STATE_DTYPE array of S entries, updated in place; tokens:
+    the S tokens emitted this step (< 0: none).  Returns (streams to restart,
+    per-stream reasons)."""
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+    if state.dtype != RESTART_STATE_DTYPE or not state.flags.c_contiguous or state.size != tok.size:
+        raise ValueError("state must be a contiguous RESTART_STATE_DTYPE array, one entry per token")
+    reason = np.zeros(tok.size, np.int32)
+    restart = np.zeros(tok.size, np.int32)
+    n = lib().rkv_restart_step(ctypes.byref(cfg), state.ctypes.data, int(tok.size),
+                               tok.ctypes.data, reason.ctypes.data, restart.ctypes.data)
+    if n < 0:
+        raise RkvError("rkv_restart_step", n)
+    return restart[:n].copy(), reason
 
 
 def rkv_workspace_bytes(cfg, slots) -> int:

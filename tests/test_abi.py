@@ -50,6 +50,8 @@ def test_struct_sizes(rkv):
     assert ctypes.sizeof(rkv.rkv_kv_view) == 64
     assert rkv.STATE_DTYPE.itemsize == 48
     assert rkv.PLAN_DTYPE.itemsize == 9344
+    assert ctypes.sizeof(rkv.rkv_restart_cfg) == 24
+    assert rkv.RESTART_STATE_DTYPE.itemsize == 24
 
 
 def test_version_and_strerror(rkv):
@@ -207,4 +209,33 @@ def test_calls_reject_bad_arguments_without_a_device(rkv):
     W1 = W + 1
     assert call(rkv, "rkv_state_init", c, F, W.ctypes.data, W1.ctypes.data, O.ctypes.data,
                 N) == rkv.RKV_ESTATE
+    assert rkv.rkv_last_hip_error() == 0
+
+
+def test_reset_streams_rejects_bad_arguments_without_a_device(rkv):
+    cfg = good_cfg(rkv)
+    c = ctypes.byref(cfg)
+    F = ctypes.c_void_p(FAKE)
+    N = None
+    S = cfg.num_streams
+    st = np.array([0, S - 1], np.int32)
+    org = np.array([0, 5], np.int64)
+    reset = lambda *a: call(rkv, "rkv_reset_streams", *a)
+    assert reset(N, F, N, 2, st.ctypes.data, org.ctypes.data, N) == rkv.RKV_EINVAL
+    assert reset(c, N, N, 2, st.ctypes.data, org.ctypes.data, N) == rkv.RKV_EINVAL
+    assert reset(c, F, N, -1, st.ctypes.data, org.ctypes.data, N) == rkv.RKV_EINVAL
+    assert reset(c, F, N, 2, N, org.ctypes.data, N) == rkv.RKV_EINVAL
+    assert reset(c, F, N, 2, st.ctypes.data, N, N) == rkv.RKV_EINVAL
+    bad = np.array([0, S], np.int32)
+    assert reset(c, F, N, 2, bad.ctypes.data, org.ctypes.data, N) == rkv.RKV_EINVAL
+    neg = np.array([-1, 0], np.int32)
+    assert reset(c, F, N, 2, neg.ctypes.data, org.ctypes.data, N) == rkv.RKV_EINVAL
+    before = np.array([0, -3], np.int64)
+    assert reset(c, F, N, 2, st.ctypes.data, before.ctypes.data, N) == rkv.RKV_ESTATE
+    assert reset(c, ctypes.c_void_p(FAKE + 4), N, 2, st.ctypes.data, org.ctypes.data,
+                 N) == rkv.RKV_EALIGN
+    assert reset(c, F, ctypes.c_void_p(FAKE + 8), 2, st.ctypes.data, org.ctypes.data,
+                 N) == rkv.RKV_EALIGN
+    # nothing to restart: no launch, no device needed
+    assert reset(c, F, N, 0, N, N, N) == rkv.RKV_OK
     assert rkv.rkv_last_hip_error() == 0
