@@ -15,7 +15,10 @@ instead of hi alone.  Attention reads hi only.
 
 With ``rounder=None`` (no rounding) the simulation must reproduce the exact
 oracle in :mod:`oracle.attention`; with bfloat16 rounding it predicts what a
-correct bf16 implementation stores.
+correct bf16 implementation stores.  V is stored in the same format: with the
+fp16 cache variant (``rounder=fp16.round_f16``; voxtral.c explainer, section
+七, fp16 KV cache) the bfloat16 inputs are rounded to fp16 on append; with
+bfloat16 storage that rounding is the identity.
 """
 from __future__ import annotations
 
@@ -30,6 +33,11 @@ from .bf16 import round_bf16
 
 def _identity(x):
     return np.asarray(x, np.float64)
+
+
+def _store(rounder, v):
+    """A V row as stored (rounded to the storage format, if any)."""
+    return (rounder or _identity)(v)
 
 
 def append_k(k_new, pos, base, compensated=False, rounder=round_bf16):
@@ -97,7 +105,7 @@ class RebaseRing:
         hi, lo = append_k(k_new, plan.pos, self.base, self.comp, self.rounder)
         self.k_hi[:, plan.slot] = hi
         self.k_lo[:, plan.slot] = lo
-        self.v[:, plan.slot] = v_new
+        self.v[:, plan.slot] = _store(self.rounder, v_new)
         q_rot = rope.rotate(q, plan.pos, self.base)
         group = self.hq // self.hkv
         out = np.empty((self.hq, self.d))
@@ -131,7 +139,7 @@ class CompactBuffer:
             self.v[:, :keep] = self.v[:, D:D + keep].copy()
         hi, _ = append_k(k_new, plan.pos, self.base, False, self.rounder)
         self.k[:, plan.slot] = hi
-        self.v[:, plan.slot] = v_new
+        self.v[:, plan.slot] = _store(self.rounder, v_new)
         n = plan.n_valid
         q_rot = rope.rotate(q, plan.pos, self.base)
         group = self.hq // self.hkv

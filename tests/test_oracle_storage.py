@@ -99,3 +99,21 @@ def test_bf16_storage_error_small_for_chunked_rebase():
         _, out = ring.step(q[t], k[t], v[t])
         err = max(err, np.max(np.abs(out - exact[t])))
     assert err < 2e-2
+
+
+def test_fp16_storage_rounds_k_and_v_in_binary16():
+    # fp16 cache variant (voxtral.c explainer, section 七): every stored K and
+    # V is a binary16 value; a V input below the binary16 normal range is
+    # rounded to its subnormal grid, and K after the append is the binary16
+    # rounding of the exact rotation.
+    from oracle import fp16, rope
+    rng = np.random.default_rng(12)
+    ring = stg.RebaseRing(2, 1, 8, 4, 2, 1e6, rounder=fp16.round_f16)
+    k = rng.standard_normal((1, 8))
+    v = np.full((1, 8), 1.0e-6)
+    q = rng.standard_normal((2, 8))
+    plan, _ = ring.step(q, k, v)
+    assert np.all(ring.v[0, plan.slot] == fp16.round_f16(1.0e-6))
+    assert np.all(ring.v[0, plan.slot] != 1.0e-6)
+    np.testing.assert_array_equal(ring.k_hi[0, plan.slot],
+                                  fp16.round_f16(rope.rotate(k, plan.pos, 1e6))[0])
