@@ -215,8 +215,9 @@ def run_gpu(c, args):
     L, S = c["L"], c["S"]
     t_setup = time.perf_counter()
     q, k, v = build_inputs(c, seed, dev)
+    kv_flags = rkv.RKV_F_KV_FP16 if args.kv_fp16 else 0
     if c["mode"] == "rebase":
-        flags = rkv.RKV_F_COMPENSATED if c.get("comp") else 0
+        flags = (rkv.RKV_F_COMPENSATED if c.get("comp") else 0) | kv_flags
         cfg = rkv.make_cfg(S, L, rebase_chunk=c["dc"], flags=flags)
         if isinstance(c["W"], tuple):
             counts = [86, 85, 85]
@@ -231,7 +232,7 @@ def run_gpu(c, args):
         cache = rkv.Cache(cfg, slots, windows, windows, origins, device=dev, zero=False)
         prefill = slots
     elif c["mode"] == "compact":
-        cfg = rkv.make_cfg(S, L, mode=rkv.RKV_MODE_COMPACT)
+        cfg = rkv.make_cfg(S, L, mode=rkv.RKV_MODE_COMPACT, flags=kv_flags)
         cache = rkv.Cache(cfg, c["cap"], c["W"], c["cap"], 0, device=dev, zero=False)
         prefill = c["cap"]
     else:
@@ -418,6 +419,8 @@ def main():
                          "rkv_append + rkv_decode_attn (encoder workloads: always "
                          "rkv_advance + rkv_encoder_chunk_attn)")
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
+    ap.add_argument("--kv-fp16", action="store_true",
+                    help="store K and V as fp16 (the fp16 cache variant; decoder workloads)")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -448,6 +451,9 @@ def main():
               "multi-GPU runs are not part of this build.", file=sys.stderr)
         sys.exit(2)
     c = dict(CONFIGS[args.config])
+    if args.kv_fp16 and c["mode"] == "enc":
+        print("--kv-fp16: the encoder cache is bfloat16 only", file=sys.stderr)
+        sys.exit(2)
     args.steps = c["steps"] if args.steps is None else args.steps
     args.warmup = c["warmup"] if args.warmup is None else args.warmup
 
@@ -462,6 +468,8 @@ def main():
               "enc": "attn_kernel<64,4,encoder_fused>"}[c["mode"]]
     if args.path == "separate" and c["mode"] != "enc":
         kernel = "rebase+append+attn_kernel<128,4,decode_read>"
+    if args.kv_fp16:
+        kernel = kernel.replace(">", ",fp16>")
     roofline = None
     if r["kernel_ms"]:
         per_launch = b_sl * L * S
@@ -485,7 +493,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16 cache, bf16 i/o" if args.kv_fp16 else "bf16",
         "data": "synthetic",
         "config": {"workload": c["name"], "layers": L, "streams": S,
                    "path": args.path if c["mode"] != "enc" else "fused",
@@ -496,7 +504,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if args.cpu:
+    if args.cpu and not args.kv_fp16:
         res["cpu_baseline"] = cpu_baseline(c, 1000 + args.config, args.cpu_budget)
     print(json.dumps(res), flush=True)
 

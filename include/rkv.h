@@ -78,7 +78,14 @@ enum {
    * rounding (needed when the base moves every step).  Attention reads hi. */
   RKV_F_COMPENSATED = 1u << 0,
   /* write attention output as float32 instead of bfloat16 */
-  RKV_F_OUT_F32 = 1u << 1
+  RKV_F_OUT_F32 = 1u << 1,
+  /* fp16 cache variant (voxtral.c explainer, section 七, "fp16 KV cache"):
+   * K, V and k_lo are stored as IEEE binary16 (11 significant bits; every
+   * stored value rounded to nearest, ties to even, from the float64 rotation
+   * or, for V, from the bfloat16 input); q, k_new, v_new stay bfloat16 and
+   * the matrix-core products run in fp16.  REBASE and COMPACT modes only
+   * (RKV_EUNSUPPORTED for ENC_CHUNK). */
+  RKV_F_KV_FP16 = 1u << 2
 };
 
 /* Problem description, shared by every call of a step (host memory). */

@@ -24,7 +24,8 @@ int check_cfg(const rkv_cfg* c) {
     return RKV_EINVAL;
   if (c->head_dim != 64 && c->head_dim != 128) return RKV_EUNSUPPORTED;
   if (c->mode < RKV_MODE_REBASE || c->mode > RKV_MODE_ENC_CHUNK) return RKV_EUNSUPPORTED;
-  if (c->flags & ~(uint32_t)(RKV_F_COMPENSATED | RKV_F_OUT_F32)) return RKV_EUNSUPPORTED;
+  if (c->flags & ~(uint32_t)(RKV_F_COMPENSATED | RKV_F_OUT_F32 | RKV_F_KV_FP16))
+    return RKV_EUNSUPPORTED;
   if (!(c->rope_base > 0.0) || !isfinite(c->rope_base)) return RKV_EINVAL;
   if (!(c->softmax_scale >= 0.0f) || !isfinite(c->softmax_scale)) return RKV_EINVAL;
   if (c->num_splits < 0) return RKV_EINVAL;
@@ -47,7 +48,7 @@ int check_cfg(const rkv_cfg* c) {
       if (c->num_q_heads != c->num_kv_heads) return RKV_EINVAL;
       if (c->new_rows < 1) return RKV_EINVAL;
       if (c->new_rows > RKV_MAX_NEW_ROWS) return RKV_EUNSUPPORTED;
-      if (c->flags & RKV_F_COMPENSATED) return RKV_EUNSUPPORTED;
+      if (c->flags & (RKV_F_COMPENSATED | RKV_F_KV_FP16)) return RKV_EUNSUPPORTED;
       break;
   }
   return RKV_OK;

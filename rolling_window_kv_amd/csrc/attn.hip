@@ -59,6 +59,35 @@ namespace rkv {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// The two matrix-core products in the cache's storage format SF (bfloat16,
+// or binary16 for the fp16 cache variant); float32 accumulation either way.
+template <typename SF>
+struct Mfma;
+template <>
+struct Mfma<StoreBf16> {
+  static __device__ __forceinline__ f32x4 scores(const u32x4& a, const u32x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(const u32x2& a, const u32x2& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<StoreF16> {
+  static __device__ __forceinline__ f32x4 scores(const u32x4& a, const u32x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(const u32x2& a, const u32x2& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+};
 
 __device__ __forceinline__ float dpp_ror8(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
@@ -81,6 +110,11 @@ struct VChunk;
 template <>
 struct VChunk<8> {
   typedef u32x4 T;
+  template <typename SF>
+  static __device__ __forceinline__ T from_input(const T& w) {
+    return T{SF::from_bf16x2(w[0]), SF::from_bf16x2(w[1]), SF::from_bf16x2(w[2]),
+             SF::from_bf16x2(w[3])};
+  }
   static __device__ __forceinline__ T load(const uint16_t* p) { return ld16_stream(p); }
   static __device__ __forceinline__ void store(uint16_t* p, const T& w) { st16(p, w); }
   static __device__ __forceinline__ T zero() { return u32x4{0u, 0u, 0u, 0u}; }
@@ -88,6 +122,10 @@ struct VChunk<8> {
 template <>
 struct VChunk<4> {
   typedef u32x2 T;
+  template <typename SF>
+  static __device__ __forceinline__ T from_input(const T& w) {
+    return T{SF::from_bf16x2(w[0]), SF::from_bf16x2(w[1])};
+  }
   static __device__ __forceinline__ T load(const uint16_t* p) { return ld8_stream(p); }
   static __device__ __forceinline__ void store(uint16_t* p, const T& w) { st8(p, w); }
   static __device__ __forceinline__ T zero() { return u32x2{0u, 0u}; }
@@ -102,7 +140,7 @@ struct Occupancy {
   static constexpr int waves = D == 128 ? (COMP ? 2 : 3) : (COMP ? 3 : 4);
 };
 
-template <int D, int NW, int KIND, bool COMP>
+template <int D, int NW, int KIND, bool COMP, typename SF>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(Occupancy<D, COMP>::waves)))
 void attn_kernel(AttnArgs a) {
@@ -269,12 +307,12 @@ void attn_kernel(AttnArgs a) {
       y1[h] = fmaf(a1, cq, -(a2 * sq));
       y2[h] = fmaf(a1, sq, a2 * cq);
     }
-    const uint32_t h1 = cvt2_bf16(y1[0], y1[1]);
-    const uint32_t h2 = cvt2_bf16(y2[0], y2[1]);
+    const uint32_t h1 = SF::cvt2(y1[0], y1[1]);
+    const uint32_t h2 = SF::cvt2(y2[0], y2[1]);
     reinterpret_cast<uint32_t*>(&sm_q[st][lane])[w] =
-        part ? cvt2_bf16(y1[0] - bf2f(h1 & 0xffffu), y1[1] - bf2f(h1 >> 16)) : h1;
+        part ? SF::cvt2(y1[0] - SF::to_f(h1 & 0xffffu), y1[1] - SF::to_f(h1 >> 16)) : h1;
     reinterpret_cast<uint32_t*>(&sm_q[st + KH][lane])[w] =
-        part ? cvt2_bf16(y2[0] - bf2f(h2 & 0xffffu), y2[1] - bf2f(h2 >> 16)) : h2;
+        part ? SF::cvt2(y2[0] - SF::to_f(h2 & 0xffffu), y2[1] - SF::to_f(h2 >> 16)) : h2;
   }
 
   // ---- fused-update parameters ----
@@ -307,18 +345,18 @@ void attn_kernel(AttnArgs a) {
           const int i = 32 * st + 8 * g4 + e;
           double x1 = bf2f(elem8(src[st], e)), x2 = bf2f(elem8(src[st + KH], e));
           if (COMP && lo) {
-            x1 += (double)bf2f(elem8(lo[st], e));
-            x2 += (double)bf2f(elem8(lo[st + KH], e));
+            x1 += (double)SF::to_f(elem8(lo[st], e));
+            x2 += (double)SF::to_f(elem8(lo[st + KH], e));
           }
           rotate_pair64(x1, x2, cs[i], sgn * sn[i], y1[h], y2[h]);
         }
-        w1[w] = cvt2_bf16_f64(y1[0], y1[1]);
-        w2[w] = cvt2_bf16_f64(y2[0], y2[1]);
+        w1[w] = SF::cvt2_f64(y1[0], y1[1]);
+        w2[w] = SF::cvt2_f64(y2[0], y2[1]);
         if (COMP) {
-          r1[w] = cvt2_bf16_f64(y1[0] - (double)bf2f(w1[w] & 0xffffu),
-                                y1[1] - (double)bf2f(w1[w] >> 16));
-          r2[w] = cvt2_bf16_f64(y2[0] - (double)bf2f(w2[w] & 0xffffu),
-                                y2[1] - (double)bf2f(w2[w] >> 16));
+          r1[w] = SF::cvt2_f64(y1[0] - (double)SF::to_f(w1[w] & 0xffffu),
+                               y1[1] - (double)SF::to_f(w1[w] >> 16));
+          r2[w] = SF::cvt2_f64(y2[0] - (double)SF::to_f(w2[w] & 0xffffu),
+                               y2[1] - (double)SF::to_f(w2[w] >> 16));
         }
       }
       st16(Kp + row * rs + 32 * st + 8 * g4, w1);
@@ -347,8 +385,8 @@ void attn_kernel(AttnArgs a) {
       for (int h = 0; h < 2; ++h)
         rotate_pair64(bf2f((kw1[k] >> (16 * h)) & 0xffffu), bf2f((kw2[k] >> (16 * h)) & 0xffffu),
                       rcs[k][h], rsn[k][h], y1[h], y2[h]);
-      const uint32_t w1 = cvt2_bf16_f64(y1[0], y1[1]);
-      const uint32_t w2 = cvt2_bf16_f64(y2[0], y2[1]);
+      const uint32_t w1 = SF::cvt2_f64(y1[0], y1[1]);
+      const uint32_t w2 = SF::cvt2_f64(y2[0], y2[1]);
       if (c == 0) {
         const int o = 32 * st + 8 * g4 + 2 * w;
         reinterpret_cast<uint32_t*>(&sm_newk[st][g4])[w] = w1;
@@ -356,16 +394,17 @@ void attn_kernel(AttnArgs a) {
         *reinterpret_cast<uint32_t*>(Kp + slot_new * rs + o) = w1;
         *reinterpret_cast<uint32_t*>(Kp + slot_new * rs + o + 32 * KH) = w2;
         if (COMP) {
-          *reinterpret_cast<uint32_t*>(Lp + slot_new * rs + o) =
-              cvt2_bf16_f64(y1[0] - (double)bf2f(w1 & 0xffffu), y1[1] - (double)bf2f(w1 >> 16));
-          *reinterpret_cast<uint32_t*>(Lp + slot_new * rs + o + 32 * KH) =
-              cvt2_bf16_f64(y2[0] - (double)bf2f(w2 & 0xffffu), y2[1] - (double)bf2f(w2 >> 16));
+          *reinterpret_cast<uint32_t*>(Lp + slot_new * rs + o) = SF::cvt2_f64(
+              y1[0] - (double)SF::to_f(w1 & 0xffffu), y1[1] - (double)SF::to_f(w1 >> 16));
+          *reinterpret_cast<uint32_t*>(Lp + slot_new * rs + o + 32 * KH) = SF::cvt2_f64(
+              y2[0] - (double)SF::to_f(w2 & 0xffffu), y2[1] - (double)SF::to_f(w2 >> 16));
         }
       }
     }
     if (wave == NW - 1 && g4 == 0) {
-      sm_newv[c] = vnew_c;
-      VC::store(Vp + slot_new * rs + CW * c, vnew_c);
+      const VT vs = VC::template from_input<SF>(vnew_c);
+      sm_newv[c] = vs;
+      VC::store(Vp + slot_new * rs + CW * c, vs);
     }
   }
 
@@ -393,7 +432,9 @@ void attn_kernel(AttnArgs a) {
         const int rv = key0 + 4 * g4 + j;
         if (rv >= ke) continue;
         const int jn = new_index(rv);
-        if (jn >= 0) VC::store(Vp + rv * rs + CW * c, VC::load(a.vnew + new_off(jn) + CW * c));
+        if (jn >= 0)
+          VC::store(Vp + rv * rs + CW * c,
+                    VC::template from_input<SF>(VC::load(a.vnew + new_off(jn) + CW * c)));
       }
     }
     load_tile(first, tb[0], lim0);
@@ -432,7 +473,7 @@ void attn_kernel(AttnArgs a) {
       for (int st = 0; st < KH; ++st) {
         const int i0 = 32 * st + 8 * g4;
         u32x4 dl = u32x4{0u, 0u, 0u, 0u}, dh = dl;
-        rebase_chunks_ff<LO>(T.k[st], T.k[st + KH], LO ? T.lo[st % (LO ? KS : 1)] : dl,
+        rebase_chunks_ff<LO, SF>(T.k[st], T.k[st + KH], LO ? T.lo[st % (LO ? KS : 1)] : dl,
                              LO ? T.lo[(st + KH) % (LO ? KS : 1)] : dh,
                              [&](int e) { return sm_dt[i0 + e]; });
       }
@@ -462,9 +503,7 @@ void attn_kernel(AttnArgs a) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < KS; ++st)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[st]),
-                                                    __builtin_bit_cast(bf16x8, sm_q[st][lane]),
-                                                    acc, 0, 0, 0);
+      acc = Mfma<SF>::scores(T.k[st], sm_q[st][lane], acc);
     float sv[4];
     float mx = -INFINITY;
 #pragma unroll
@@ -501,13 +540,13 @@ void attn_kernel(AttnArgs a) {
       for (int w = 0; w < CW / 2; ++w) T.v[j][w] = live ? T.v[j][w] : 0u;
     }
     l_run += (pj[0] + pj[1]) + (pj[2] + pj[3]);
-    const uint32_t h01 = cvt2_bf16(pj[0], pj[1]);
-    const uint32_t h23 = cvt2_bf16(pj[2], pj[3]);
-    const uint32_t l01 = cvt2_bf16(pj[0] - bf2f(h01 & 0xffffu), pj[1] - bf2f(h01 >> 16));
-    const uint32_t l23 = cvt2_bf16(pj[2] - bf2f(h23 & 0xffffu), pj[3] - bf2f(h23 >> 16));
+    const uint32_t h01 = SF::cvt2(pj[0], pj[1]);
+    const uint32_t h23 = SF::cvt2(pj[2], pj[3]);
+    const uint32_t l01 = SF::cvt2(pj[0] - SF::to_f(h01 & 0xffffu), pj[1] - SF::to_f(h01 >> 16));
+    const uint32_t l23 = SF::cvt2(pj[2] - SF::to_f(h23 & 0xffffu), pj[3] - SF::to_f(h23 >> 16));
     const uint32_t p01 = part ? l01 : h01;
     const uint32_t p23 = part ? l23 : h23;
-    const s16x4 pop = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+    const u32x2 pop = u32x2{p01, p23};
 
     // V^T operand: dims CW*c + e of the tile's 4 keys of this lane group
 #pragma unroll
@@ -515,8 +554,7 @@ void attn_kernel(AttnArgs a) {
       const int wd = e >> 1;
       const uint32_t w0 = (e & 1) ? pack_hi(T.v[0][wd], T.v[1][wd]) : pack_lo(T.v[0][wd], T.v[1][wd]);
       const uint32_t w1 = (e & 1) ? pack_hi(T.v[2][wd], T.v[3][wd]) : pack_lo(T.v[2][wd], T.v[3][wd]);
-      oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{w0, w1}),
-                                                           pop, oacc[e], 0, 0, 0);
+      oacc[e] = Mfma<SF>::pv(u32x2{w0, w1}, pop, oacc[e]);
     }
   };
 
@@ -675,10 +713,10 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
 
 constexpr int kWavesPerGroup = 4;
 
-template <int D, int KIND, bool COMP>
+template <int D, int KIND, bool COMP, typename SF>
 hipError_t launch_kind(const AttnArgs& args, int items, hipStream_t stream) {
   const int extra = args.adv_state ? (args.S + kWavesPerGroup - 1) / kWavesPerGroup : 0;
-  hipLaunchKernelGGL((attn_kernel<D, kWavesPerGroup, KIND, COMP>),
+  hipLaunchKernelGGL((attn_kernel<D, kWavesPerGroup, KIND, COMP, SF>),
                      dim3(items * args.nsplit + extra), dim3(kWavesPerGroup * 64), 0, stream,
                      args);
   hipError_t e = hipGetLastError();
@@ -687,18 +725,22 @@ hipError_t launch_kind(const AttnArgs& args, int items, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, typename SF>
+hipError_t launch_dec(AttnKind kind, bool comp, const AttnArgs& args, int items,
+                      hipStream_t stream) {
+  if (kind == kDecodeRead) return launch_kind<D, kDecodeRead, false, SF>(args, items, stream);
+  return comp ? launch_kind<D, kDecodeFused, true, SF>(args, items, stream)
+              : launch_kind<D, kDecodeFused, false, SF>(args, items, stream);
+}
+
 template <int D>
-hipError_t launch_d(AttnKind kind, bool comp, const AttnArgs& args, int items,
+hipError_t launch_d(AttnKind kind, bool comp, bool f16, const AttnArgs& args, int items,
                     hipStream_t stream) {
-  switch (kind) {
-    case kDecodeRead:
-      return launch_kind<D, kDecodeRead, false>(args, items, stream);
-    case kDecodeFused:
-      return comp ? launch_kind<D, kDecodeFused, true>(args, items, stream)
-                  : launch_kind<D, kDecodeFused, false>(args, items, stream);
-    default:
-      return launch_kind<D, kEncoderFused, false>(args, items, stream);
-  }
+  // the encoder stores bfloat16 only (the configuration check rejects fp16)
+  if (kind == kEncoderFused)
+    return launch_kind<D, kEncoderFused, false, StoreBf16>(args, items, stream);
+  return f16 ? launch_dec<D, StoreF16>(kind, comp, args, items, stream)
+             : launch_dec<D, StoreBf16>(kind, comp, args, items, stream);
 }
 
 }  // namespace
@@ -722,8 +764,9 @@ hipError_t launch_attention(const rkv_cfg* cfg, AttnKind kind, const AttnArgs& a
                             hipStream_t stream) {
   const int items = cfg->num_layers * cfg->num_streams * cfg->num_kv_heads;
   const bool comp = (cfg->flags & RKV_F_COMPENSATED) != 0;
-  if (cfg->head_dim == 128) return launch_d<128>(kind, comp, args, items, stream);
-  return launch_d<64>(kind, comp, args, items, stream);
+  const bool f16 = (cfg->flags & RKV_F_KV_FP16) != 0;
+  if (cfg->head_dim == 128) return launch_d<128>(kind, comp, f16, args, items, stream);
+  return launch_d<64>(kind, comp, f16, args, items, stream);
 }
 
 }  // namespace rkv

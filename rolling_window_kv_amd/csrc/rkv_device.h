@@ -62,6 +62,54 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double y) {
   return f2bf(f64_for_bf16(y));
 }
 
+// float64 -> float32 rounded to odd: truncated toward zero, with the last bit
+// set when the conversion is inexact.  Rounding that float32 to nearest in a
+// format of at most 22 significant bits gives the correctly rounded float64
+// value (the sticky bit keeps the float64 value's side of every tie).
+__device__ __forceinline__ float f64_to_f32_odd(double y) {
+  const float t = (float)y;
+  const double back = (double)t;
+  if (back == y) return t;
+  uint32_t u = __float_as_uint(t);
+  if (fabs(back) > fabs(y)) u -= 1u;   // rounded away from zero: one step back
+  return __uint_as_float(u | 1u);
+}
+
+// Storage formats of the cache's 16-bit words (K, V, the K residual):
+// bfloat16, or IEEE binary16 for the fp16 cache variant (voxtral.c explainer,
+// section 七).  to_f widens a stored word; cvt2 rounds two floats to nearest
+// (ties to even) and packs them (low half = a); cvt2_f64 / from_f64 round
+// float64 values correctly; from_bf16x2 converts two packed bfloat16 inputs.
+struct StoreBf16 {
+  static __device__ __forceinline__ float to_f(uint32_t h) { return bf2f(h); }
+  static __device__ __forceinline__ uint32_t cvt2(float a, float b) { return cvt2_bf16(a, b); }
+  static __device__ __forceinline__ uint32_t cvt2_f64(double a, double b) {
+    return cvt2_bf16_f64(a, b);
+  }
+  static __device__ __forceinline__ uint32_t from_f64(double y) { return f64_to_bf16(y); }
+  static __device__ __forceinline__ uint32_t from_bf16x2(uint32_t w) { return w; }
+};
+
+struct StoreF16 {
+  static __device__ __forceinline__ float to_f(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  }
+  static __device__ __forceinline__ uint32_t cvt2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
+  }
+  static __device__ __forceinline__ uint32_t cvt2_f64(double a, double b) {
+    return cvt2(f64_to_f32_odd(a), f64_to_f32_odd(b));
+  }
+  static __device__ __forceinline__ uint32_t from_f64(double y) {
+    return cvt2(f64_to_f32_odd(y), 0.f) & 0xffffu;
+  }
+  static __device__ __forceinline__ uint32_t from_bf16x2(uint32_t w) {
+    return cvt2(bf2f(w & 0xffffu), bf2f(w >> 16));
+  }
+};
+
 // Rotation of one pair in float64: y1 = x1 c - x2 s, y2 = x1 s + x2 c.
 __device__ __forceinline__ void rotate_pair64(double x1, double x2, double c, double s,
                                               double& y1, double& y2) {
@@ -115,11 +163,11 @@ __device__ __forceinline__ void rotate_pair_ff(float x1, float x2, float ch, flo
 // Re-base one chunk pair of a K row by R(-D): a holds dims i0 .. i0+7 and b
 // dims i0 + d/2 .. (the rotary partners); table(e) returns {ch, cl, sh, sl} of
 // pair i0 + e, the float32 hi/lo split of cos(D theta) and -sin(D theta).
-// Inputs are exact in float32 (bfloat16, or hi + lo with at most 16
-// significant bits); each result is rounded to nearest bfloat16.
-// Compensated: la / lb hold the residuals; x = hi + lo is rotated and split
-// again into hi and lo.
-template <bool COMP, typename Table>
+// Inputs are exact in float32 (one stored word, or hi + lo with at most 22
+// significant bits); each result is rounded to nearest in the storage format
+// SF.  Compensated: la / lb hold the residuals; x = hi + lo is rotated and
+// split again into hi and lo.
+template <bool COMP, typename SF, typename Table>
 __device__ __forceinline__ void rebase_chunks_ff(u32x4& a, u32x4& b, u32x4& la, u32x4& lb,
                                                  Table table) {
   u32x4 na, nb, nla, nlb;
@@ -130,20 +178,20 @@ __device__ __forceinline__ void rebase_chunks_ff(u32x4& a, u32x4& b, u32x4& la, 
     for (int h = 0; h < 2; ++h) {
       const int e = 2 * w + h;
       const int sh = 16 * h;
-      float x1 = __uint_as_float(((a[w] >> sh) & 0xffffu) << 16);
-      float x2 = __uint_as_float(((b[w] >> sh) & 0xffffu) << 16);
+      float x1 = SF::to_f((a[w] >> sh) & 0xffffu);
+      float x2 = SF::to_f((b[w] >> sh) & 0xffffu);
       if (COMP) {
-        x1 += __uint_as_float(((la[w] >> sh) & 0xffffu) << 16);
-        x2 += __uint_as_float(((lb[w] >> sh) & 0xffffu) << 16);
+        x1 += SF::to_f((la[w] >> sh) & 0xffffu);
+        x2 += SF::to_f((lb[w] >> sh) & 0xffffu);
       }
       const f32x4 t = table(e);
       rotate_pair_ff(x1, x2, t[0], t[1], t[2], t[3], y1[h], y2[h]);
     }
-    na[w] = cvt2_bf16(y1[0], y1[1]);
-    nb[w] = cvt2_bf16(y2[0], y2[1]);
+    na[w] = SF::cvt2(y1[0], y1[1]);
+    nb[w] = SF::cvt2(y2[0], y2[1]);
     if (COMP) {
-      nla[w] = cvt2_bf16(y1[0] - bf2f(na[w] & 0xffffu), y1[1] - bf2f(na[w] >> 16));
-      nlb[w] = cvt2_bf16(y2[0] - bf2f(nb[w] & 0xffffu), y2[1] - bf2f(nb[w] >> 16));
+      nla[w] = SF::cvt2(y1[0] - SF::to_f(na[w] & 0xffffu), y1[1] - SF::to_f(na[w] >> 16));
+      nlb[w] = SF::cvt2(y2[0] - SF::to_f(nb[w] & 0xffffu), y2[1] - SF::to_f(nb[w] >> 16));
     }
   }
   a = na;

@@ -17,7 +17,7 @@ __device__ __forceinline__ void item_coords(int item, int H, int S, int& l, int&
 // in).  One wave per (layer, stream, kv head, new row); lane i owns rotary
 // pair i (elements i and i + d/2) and V elements 2i, 2i+1.
 // ---------------------------------------------------------------------------
-template <int D, bool COMP, bool ENC>
+template <int D, bool COMP, bool ENC, typename SF>
 __global__ __launch_bounds__(64) void append_kernel(const rkv_step_plan* __restrict__ plan,
                                                     RingArgs ring,
                                                     const uint16_t* __restrict__ knew,
@@ -41,27 +41,28 @@ __global__ __launch_bounds__(64) void append_kernel(const rkv_step_plan* __restr
     const double x2 = bf2f(knew[in_off + i + HALF]);
     double y1, y2;
     rotate_pair64(x1, x2, P->rope_new[j][0][i], P->rope_new[j][1][i], y1, y2);
-    const uint32_t h1 = f64_to_bf16(y1), h2 = f64_to_bf16(y2);
+    const uint32_t h1 = SF::from_f64(y1), h2 = SF::from_f64(y2);
     ring.k[row + i] = (uint16_t)h1;
     ring.k[row + i + HALF] = (uint16_t)h2;
     if (COMP) {
-      ring.klo[row + i] = (uint16_t)f64_to_bf16(y1 - (double)bf2f(h1));
-      ring.klo[row + i + HALF] = (uint16_t)f64_to_bf16(y2 - (double)bf2f(h2));
+      ring.klo[row + i] = (uint16_t)SF::from_f64(y1 - (double)SF::to_f(h1));
+      ring.klo[row + i + HALF] = (uint16_t)SF::from_f64(y2 - (double)SF::to_f(h2));
     }
     const uint32_t vv = *reinterpret_cast<const uint32_t*>(vnew + in_off + 2 * i);
-    *reinterpret_cast<uint32_t*>(ring.v + row + 2 * i) = vv;
+    *reinterpret_cast<uint32_t*>(ring.v + row + 2 * i) = SF::from_bf16x2(vv);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Exact re-base (Audio8 explainer, "Rolling KV Cache 三步拆解" step 2): every
 // retained K row is rotated by R(-D) in place (float32 with hi/lo tables and
-// exact product errors, rounded to nearest bfloat16: within 1 ulp of the
-// correctly rounded rotation; the same arithmetic as the fused decode step).
+// exact product errors, rounded to nearest in the storage format: within 1
+// ulp of the correctly rounded rotation; the same arithmetic as the fused
+// decode step).
 // One block per (layer, stream, head) item; a thread owns 8 rotary pairs of a
 // row (16 bytes from each half) and walks the item's rows.
 // ---------------------------------------------------------------------------
-template <int D, bool COMP>
+template <int D, bool COMP, typename SF>
 __global__ __launch_bounds__(256) void rebase_kernel(const rkv_step_plan* __restrict__ plan,
                                                      RingArgs ring, int S, int H) {
   constexpr int HALF = D / 2;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void rebase_kernel(const rkv_step_plan* __rest
       la = ld16(ring.klo + row + 8 * c);
       lb = ld16(ring.klo + row + 8 * c + HALF);
     }
-    rebase_chunks_ff<COMP>(a, b, la, lb, [&](int e) { return tab[e]; });
+    rebase_chunks_ff<COMP, SF>(a, b, la, lb, [&](int e) { return tab[e]; });
     st16(k1, a);
     st16(k2, b);
     if (COMP) {
@@ -151,19 +152,23 @@ hipError_t launch_append(const rkv_cfg* cfg, const rkv_step_plan* plan, const Ri
   const dim3 grid(L * S * H, cfg->new_rows);
   const bool comp = (cfg->flags & RKV_F_COMPENSATED) != 0;
   const bool enc = cfg->mode == RKV_MODE_ENC_CHUNK;
+  const bool f16 = (cfg->flags & RKV_F_KV_FP16) != 0;
   const int F = cfg->new_rows;
-#define RKV_APPEND(DD, CC, EE)                                                                  \
-  hipLaunchKernelGGL((append_kernel<DD, CC, EE>), grid, dim3(64), 0, stream, plan, ring, knew, \
-                     vnew, S, H, F)
+#define RKV_APPEND(DD, CC, EE, SS)                                                             \
+  hipLaunchKernelGGL((append_kernel<DD, CC, EE, SS>), grid, dim3(64), 0, stream, plan, ring, \
+                     knew, vnew, S, H, F)
+#define RKV_APPEND_D(DD)                                 \
+  if (enc) RKV_APPEND(DD, false, true, StoreBf16);       \
+  else if (comp && f16) RKV_APPEND(DD, true, false, StoreF16);  \
+  else if (comp) RKV_APPEND(DD, true, false, StoreBf16); \
+  else if (f16) RKV_APPEND(DD, false, false, StoreF16);  \
+  else RKV_APPEND(DD, false, false, StoreBf16)
   if (cfg->head_dim == 128) {
-    if (enc) RKV_APPEND(128, false, true);
-    else if (comp) RKV_APPEND(128, true, false);
-    else RKV_APPEND(128, false, false);
+    RKV_APPEND_D(128);
   } else {
-    if (enc) RKV_APPEND(64, false, true);
-    else if (comp) RKV_APPEND(64, true, false);
-    else RKV_APPEND(64, false, false);
+    RKV_APPEND_D(64);
   }
+#undef RKV_APPEND_D
 #undef RKV_APPEND
   return hipGetLastError();
 }
@@ -172,14 +177,22 @@ hipError_t launch_rebase(const rkv_cfg* cfg, const rkv_step_plan* plan, const Ri
                          hipStream_t stream) {
   const int S = cfg->num_streams, H = cfg->num_kv_heads, L = cfg->num_layers;
   const bool comp = (cfg->flags & RKV_F_COMPENSATED) != 0;
+  const bool f16 = (cfg->flags & RKV_F_KV_FP16) != 0;
   const dim3 grid(L * S * H);
+#define RKV_REBASE(DD, CC, SS) \
+  hipLaunchKernelGGL((rebase_kernel<DD, CC, SS>), grid, dim3(256), 0, stream, plan, ring, S, H)
+#define RKV_REBASE_D(DD)                                    \
+  if (comp && f16) RKV_REBASE(DD, true, StoreF16);          \
+  else if (comp) RKV_REBASE(DD, true, StoreBf16);           \
+  else if (f16) RKV_REBASE(DD, false, StoreF16);            \
+  else RKV_REBASE(DD, false, StoreBf16)
   if (cfg->head_dim == 128) {
-    if (comp) hipLaunchKernelGGL((rebase_kernel<128, true>), grid, dim3(256), 0, stream, plan, ring, S, H);
-    else hipLaunchKernelGGL((rebase_kernel<128, false>), grid, dim3(256), 0, stream, plan, ring, S, H);
+    RKV_REBASE_D(128);
   } else {
-    if (comp) hipLaunchKernelGGL((rebase_kernel<64, true>), grid, dim3(256), 0, stream, plan, ring, S, H);
-    else hipLaunchKernelGGL((rebase_kernel<64, false>), grid, dim3(256), 0, stream, plan, ring, S, H);
+    RKV_REBASE_D(64);
   }
+#undef RKV_REBASE_D
+#undef RKV_REBASE
   return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@ RKV_MODE_ENC_CHUNK = 2
 
 RKV_F_COMPENSATED = 1
 RKV_F_OUT_F32 = 2
+RKV_F_KV_FP16 = 4
 
 RKV_MAX_NEW_ROWS = 8
 RKV_MAX_HEAD_DIM = 128
@@ -365,18 +366,20 @@ class Cache:
         self.cfg = cfg
         L, S, H, d = cfg.num_layers, cfg.num_streams, cfg.num_kv_heads, cfg.head_dim
         comp = bool(cfg.flags & RKV_F_COMPENSATED)
+        # storage format of K, V, k_lo: bfloat16, or binary16 (RKV_F_KV_FP16)
+        dt = torch.float16 if cfg.flags & RKV_F_KV_FP16 else torch.bfloat16
         alloc = torch.zeros if zero else torch.empty
         if layout == "interleaved":
             n = 3 if comp else 2
-            self.buf = alloc((L, S, H, slots, n, d), dtype=torch.bfloat16, device=device)
+            self.buf = alloc((L, S, H, slots, n, d), dtype=dt, device=device)
             self.k = self.buf[:, :, :, :, 0, :]
             self.v = self.buf[:, :, :, :, 1, :]
             self.k_lo = self.buf[:, :, :, :, 2, :] if comp else None
         elif layout == "separate":
             shape = (L, S, H, slots, d)
-            self.k = alloc(shape, dtype=torch.bfloat16, device=device)
-            self.v = alloc(shape, dtype=torch.bfloat16, device=device)
-            self.k_lo = alloc(shape, dtype=torch.bfloat16, device=device) if comp else None
+            self.k = alloc(shape, dtype=dt, device=device)
+            self.v = alloc(shape, dtype=dt, device=device)
+            self.k_lo = alloc(shape, dtype=dt, device=device) if comp else None
         else:
             raise ValueError(layout)
         self.kv = kv_view(self.k, self.v, self.k_lo)

@@ -239,3 +239,17 @@ def test_reset_streams_rejects_bad_arguments_without_a_device(rkv):
     # nothing to restart: no launch, no device needed
     assert reset(c, F, N, 0, N, N, N) == rkv.RKV_OK
     assert rkv.rkv_last_hip_error() == 0
+
+
+def test_fp16_cache_flag(rkv):
+    ok = good_cfg(rkv, flags=rkv.RKV_F_KV_FP16)
+    assert rkv.lib().rkv_validate_cfg(ctypes.byref(ok)) == rkv.RKV_OK
+    both = good_cfg(rkv, flags=rkv.RKV_F_KV_FP16 | rkv.RKV_F_COMPENSATED)
+    assert rkv.lib().rkv_validate_cfg(ctypes.byref(both)) == rkv.RKV_OK
+    comp = rkv.make_cfg(2, 1, mode=rkv.RKV_MODE_COMPACT, flags=rkv.RKV_F_KV_FP16)
+    assert rkv.lib().rkv_validate_cfg(ctypes.byref(comp)) == rkv.RKV_OK
+    enc = rkv.make_cfg(2, 1, num_q_heads=4, num_kv_heads=4, head_dim=64,
+                       mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=4, flags=rkv.RKV_F_KV_FP16)
+    assert rkv.lib().rkv_validate_cfg(ctypes.byref(enc)) == rkv.RKV_EUNSUPPORTED
+    unknown = good_cfg(rkv, flags=1 << 3)
+    assert rkv.lib().rkv_validate_cfg(ctypes.byref(unknown)) == rkv.RKV_EUNSUPPORTED
