@@ -355,6 +355,50 @@ def run_gpu(c, args):
                 setup_s=setup_s, prefill=prefill)
 
 
+def run_mel(args):
+    """The rolling log-mel front end (rkv_mel_step): S streams, one step of
+    1280 samples (80 ms at 16 kHz) per call, 8 frames of 128 mel bands each.
+    Reported against the float32 vector peak with the direct DFT's flops
+    (4 per sample and bin, plus 2 per bin and band)."""
+    import torch
+    from rolling_window_kv_amd import rkv
+    S = args.mel
+    steps = args.steps or 200
+    warm = args.warmup if args.warmup is not None else 10
+    cfg = rkv.make_mel_cfg(S)
+    dev = torch.device("cuda:0")
+    fe = rkv.MelFrontend(cfg, device=dev)
+    gen = torch.Generator().manual_seed(6)
+    P = 8
+    x = (torch.randn((P, S, cfg.samples_per_step), generator=gen) * 0.1).to(dev)
+    out = torch.empty((S, cfg.samples_per_step // cfg.hop, cfg.n_mels), device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warm):
+        fe.step(x[i % P], out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        fe.step(x[i % P], out)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    frames = S * (cfg.samples_per_step // cfg.hop)
+    bins = cfg.n_fft // 2 + 1
+    flops = frames * (4.0 * cfg.n_fft * bins + 2.0 * bins * cfg.n_mels)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"metric": "log-mel frames/s (rolling front end)", "value": round(frames / ms * 1e3, 1),
+            "unit": "frames/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"rolling log-mel front end: {S} streams, 1280 samples per "
+                                   "step (80 ms at 16 kHz), n_fft 400, hop 160, 128 mel"},
+            "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": 157.3,
+                         "unit": "TFLOP/s", "frac": round(tflops / 157.3, 4), "traffic": None,
+                         "kernel": "mel_kernel", "flops_per_step": flops},
+            "cpu_baseline": None}
+
+
 def summarize_rocprof(root, last=0):
     """Per-kernel figures from a rocprofv3 CSV output folder: its own --stats
     table, mean dispatch duration from the kernel trace (and, with last > 0,
@@ -419,6 +463,8 @@ def main():
                          "rkv_append + rkv_decode_attn (encoder workloads: always "
                          "rkv_advance + rkv_encoder_chunk_attn)")
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
+    ap.add_argument("--mel", type=int, default=0, metavar="STREAMS",
+                    help="time the rolling log-mel front end for STREAMS streams instead")
     ap.add_argument("--kv-fp16", action="store_true",
                     help="store K and V as fp16 (the fp16 cache variant; decoder workloads)")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
@@ -450,6 +496,9 @@ def main():
               "run the same per-GPU workload on their own streams with no communication; "
               "multi-GPU runs are not part of this build.", file=sys.stderr)
         sys.exit(2)
+    if args.mel:
+        print(json.dumps(run_mel(args)), flush=True)
+        return
     c = dict(CONFIGS[args.config])
     if args.kv_fp16 and c["mode"] == "enc":
         print("--kv-fp16: the encoder cache is bfloat16 only", file=sys.stderr)

@@ -349,6 +349,51 @@ int rkv_restart_step(const rkv_restart_cfg* cfg, rkv_restart_state* h_state,
                      int32_t num_streams, const int32_t* h_token, int32_t* h_reason,
                      int32_t* h_restart);
 
+/* ---------------------------------------------------------------------------
+ * Rolling log-mel front end (voxtral.c explainer, section 三: the mel buffer
+ * rolls too -- audio samples that can no longer contribute to a future mel
+ * frame are dropped -- so every stage runs in bounded memory).  The Audio8
+ * explainer's file table gives the features: 16 kHz, 128 mel bands, hop 160
+ * samples; one step of the 80 ms clock carries 1280 samples.
+ * ------------------------------------------------------------------------- */
+
+#define RKV_MEL_MAX_FFT 512
+
+typedef struct rkv_mel_cfg {
+  int32_t num_streams;       /* S >= 1 */
+  int32_t n_fft;             /* analysis window in samples, hop <= n_fft <= RKV_MEL_MAX_FFT (400) */
+  int32_t hop;               /* frame step in samples, >= 1 (160) */
+  int32_t n_mels;            /* mel bands, 1 .. 1024 (128) */
+  int32_t samples_per_step;  /* a multiple of hop and >= n_fft - hop (1280 at the 80 ms clock) */
+  int32_t reserved;
+} rkv_mel_cfg;
+
+/* Slaney-scale triangular mel filterbank (linear below 1 kHz, logarithmic
+ * above; filters spanning 0 Hz .. sample_rate / 2, each scaled by 2 / its
+ * width in Hz) for bins k = 0 .. n_fft/2 at k * sample_rate / n_fft:
+ * h_filters[n_mels][n_fft/2 + 1] (host, float32; float64 arithmetic).
+ * RKV_EINVAL on a bad cfg, null pointer or sample_rate <= 0. */
+int rkv_mel_filters_host(const rkv_mel_cfg* cfg, double sample_rate, float* h_filters);
+
+/* One step of the rolling front end for every stream s.  The stream's buffer
+ * is d_tail_in[s] (n_fft - hop samples kept from the previous step; zeros for
+ * a new stream, which thus starts after n_fft - hop silent samples) followed
+ * by d_samples[s] (samples_per_step new float32 samples).  For frames
+ * f < samples_per_step / hop the frame is the buffer's samples
+ * [f*hop, f*hop + n_fft) times the periodic Hann window
+ * 0.5 - 0.5 cos(2 pi n / n_fft); out[s][f][m] =
+ * log10(max(sum_k filters[m][k] |DFT_k(frame)|^2, 1e-10)) (float32; DFT sums
+ * in float32).  d_tail_out[s] receives the n_fft - hop newest samples, all a
+ * later frame can use.  Layouts: tails [S][n_fft - hop], samples
+ * [S][samples_per_step], filters [n_mels][n_fft/2 + 1], out
+ * [S][samples_per_step / hop][n_mels], all float32 device memory, 4-byte
+ * aligned; d_tail_in and d_tail_out must not overlap (callers alternate two
+ * buffers).  Asynchronous; no allocation.  RKV_EINVAL on a bad cfg, null
+ * pointer or overlapping tails, RKV_EALIGN on misaligned pointers. */
+int rkv_mel_step(const rkv_mel_cfg* cfg, const float* d_tail_in, float* d_tail_out,
+                 const float* d_samples, const float* d_filters, float* d_out,
+                 void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

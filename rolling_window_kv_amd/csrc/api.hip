@@ -258,6 +258,65 @@ int rkv_reset_streams(const rkv_cfg* cfg, rkv_stream_state* d_state, rkv_step_pl
   return RKV_OK;
 }
 
+static int check_mel(const rkv_mel_cfg* c) {
+  if (!c) return RKV_EINVAL;
+  if (c->num_streams < 1 || c->hop < 1 || c->n_fft < c->hop || c->n_fft > RKV_MEL_MAX_FFT)
+    return RKV_EINVAL;
+  if (c->n_mels < 1 || c->n_mels > 1024) return RKV_EINVAL;
+  if (c->samples_per_step < 1 || c->samples_per_step % c->hop ||
+      c->samples_per_step < c->n_fft - c->hop)
+    return RKV_EINVAL;
+  const int64_t frames = (int64_t)c->num_streams * (c->samples_per_step / c->hop);
+  if (c->samples_per_step / c->hop > 65535 || frames > ((int64_t)1 << 31)) return RKV_EINVAL;
+  return RKV_OK;
+}
+
+int rkv_mel_filters_host(const rkv_mel_cfg* cfg, double sample_rate, float* h_filters) {
+  int rc = check_mel(cfg);
+  if (rc) return rc;
+  if (!h_filters || !(sample_rate > 0.0) || !isfinite(sample_rate)) return RKV_EINVAL;
+  // Slaney mel scale: 200/3 Hz per mel up to 1 kHz (15 mel), then a fixed
+  // ratio of 6.4 per 27 mel.
+  const double f_sp = 200.0 / 3.0, min_log_hz = 1000.0, min_log_mel = min_log_hz / f_sp;
+  const double step = log(6.4) / 27.0;
+  auto to_mel = [&](double f) {
+    return f < min_log_hz ? f / f_sp : min_log_mel + log(f / min_log_hz) / step;
+  };
+  auto to_hz = [&](double m) {
+    return m < min_log_mel ? m * f_sp : min_log_hz * exp(step * (m - min_log_mel));
+  };
+  const int bins = cfg->n_fft / 2 + 1;
+  const double top = to_mel(sample_rate / 2.0);
+  for (int b = 0; b < cfg->n_mels; ++b) {
+    const double lo = to_hz(top * b / (cfg->n_mels + 1));
+    const double mid = to_hz(top * (b + 1) / (cfg->n_mels + 1));
+    const double hi = to_hz(top * (b + 2) / (cfg->n_mels + 1));
+    const double scale = 2.0 / (hi - lo);
+    for (int k = 0; k < bins; ++k) {
+      const double f = k * sample_rate / cfg->n_fft;
+      const double up = (f - lo) / (mid - lo), down = (hi - f) / (hi - mid);
+      const double t = up < down ? up : down;
+      h_filters[(int64_t)b * bins + k] = (float)((t > 0.0 ? t : 0.0) * scale);
+    }
+  }
+  return RKV_OK;
+}
+
+int rkv_mel_step(const rkv_mel_cfg* cfg, const float* d_tail_in, float* d_tail_out,
+                 const float* d_samples, const float* d_filters, float* d_out,
+                 void* hip_stream) {
+  int rc = check_mel(cfg);
+  if (rc) return rc;
+  if (!d_tail_in || !d_tail_out || !d_samples || !d_filters || !d_out) return RKV_EINVAL;
+  const uintptr_t a = (uintptr_t)d_tail_in, b = (uintptr_t)d_tail_out;
+  const uintptr_t bytes = (uintptr_t)cfg->num_streams * (cfg->n_fft - cfg->hop) * sizeof(float);
+  if (bytes && a < b + bytes && b < a + bytes) return RKV_EINVAL;
+  if ((a | b | (uintptr_t)d_samples | (uintptr_t)d_filters | (uintptr_t)d_out) & 3u)
+    return RKV_EALIGN;
+  return hip_status(rkv::launch_mel(cfg, d_tail_in, d_tail_out, d_samples, d_filters, d_out,
+                                    static_cast<hipStream_t>(hip_stream)));
+}
+
 size_t rkv_workspace_bytes(const rkv_cfg* cfg, int32_t slots) {
   if (check_cfg(cfg) || slots < 1) return 0;
   return workspace_for(cfg, slots);

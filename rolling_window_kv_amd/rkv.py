@@ -41,6 +41,7 @@ ENTRY_POINTS = (
     "rkv_roll_rebase", "rkv_compact", "rkv_decode_attn", "rkv_decode_step",
     "rkv_decode_step_pipelined",
     "rkv_encoder_chunk_attn", "rkv_reset_streams", "rkv_restart_step",
+    "rkv_mel_filters_host", "rkv_mel_step",
 )
 
 RKV_STREAM_MAX_DECODE_KV = 2000
@@ -78,6 +79,14 @@ class rkv_kv_view(ctypes.Structure):
         ("layer_stride", ctypes.c_int64), ("stream_stride", ctypes.c_int64),
         ("head_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
         ("slots", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class rkv_mel_cfg(ctypes.Structure):
+    _fields_ = [
+        ("num_streams", ctypes.c_int32), ("n_fft", ctypes.c_int32), ("hop", ctypes.c_int32),
+        ("n_mels", ctypes.c_int32), ("samples_per_step", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -141,6 +150,10 @@ def lib():
             "rkv_reset_streams": ([pc, vp, vp, i32, vp, vp, vp], ctypes.c_int),
             "rkv_restart_step": ([ctypes.POINTER(rkv_restart_cfg), vp, i32, vp, vp, vp],
                                  ctypes.c_int),
+            "rkv_mel_filters_host": ([ctypes.POINTER(rkv_mel_cfg), ctypes.c_double, vp],
+                                     ctypes.c_int),
+            "rkv_mel_step": ([ctypes.POINTER(rkv_mel_cfg), vp, vp, vp, vp, vp, vp],
+                             ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -280,6 +293,46 @@ def rkv_restart_step(cfg, state, tokens):
     if n < 0:
         raise RkvError("rkv_restart_step", n)
     return restart[:n].copy(), reason
+
+
+def make_mel_cfg(num_streams, n_fft=400, hop=160, n_mels=128,
+                 samples_per_step=1280) -> rkv_mel_cfg:
+    return rkv_mel_cfg(num_streams, n_fft, hop, n_mels, samples_per_step, 0)
+
+
+def rkv_mel_filters_host(cfg, sample_rate=16000.0) -> np.ndarray:
+    """[n_mels, n_fft // 2 + 1] float32 mel filterbank (host)."""
+    out = np.zeros((cfg.n_mels, cfg.n_fft // 2 + 1), np.float32)
+    _check("rkv_mel_filters_host",
+           lib().rkv_mel_filters_host(ctypes.byref(cfg), float(sample_rate), out.ctypes.data))
+    return out
+
+
+def rkv_mel_step(cfg, tail_in, tail_out, samples, filters, out, stream=None):
+    _check("rkv_mel_step", lib().rkv_mel_step(ctypes.byref(cfg), _ptr(tail_in), _ptr(tail_out),
+                                              _ptr(samples), _ptr(filters), _ptr(out),
+                                              _stream(stream)))
+
+
+class MelFrontend:
+    """Device buffers of the rolling log-mel front end: two alternating sample
+    tails (zero: every stream starts after n_fft - hop silent samples) and the
+    filterbank."""
+
+    def __init__(self, cfg, sample_rate=16000.0, device="cuda"):
+        import torch
+        self.cfg = cfg
+        keep = cfg.n_fft - cfg.hop
+        self.tails = [torch.zeros((cfg.num_streams, keep), dtype=torch.float32, device=device)
+                      for _ in range(2)]
+        self.filters = torch.from_numpy(rkv_mel_filters_host(cfg, sample_rate)).to(device)
+        self.parity = 0
+
+    def step(self, samples, out, stream=None):
+        """samples [S, samples_per_step] -> out [S, samples_per_step // hop, n_mels]."""
+        a, b = self.tails[self.parity], self.tails[1 - self.parity]
+        rkv_mel_step(self.cfg, a, b, samples, self.filters, out, stream)
+        self.parity = 1 - self.parity
 
 
 def rkv_workspace_bytes(cfg, slots) -> int:
