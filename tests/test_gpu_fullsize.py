@@ -1,13 +1,15 @@
-"""Full-size workloads in the launch configuration bench.py times (fused
-rkv_decode_step / rkv_encoder_chunk_attn over all layers in one launch, the
-same input pools), checked on sampled (layer, stream) outputs that the oracle
-computes one by one, plus properties that hold at any size (every plan
-bit-exact against the oracle schedule, all outputs finite)."""
+"""Full-size workloads in the launch configuration bench.py times (one
+rkv_decode_step_pipelined launch per step over all layers, plans alternating
+between two buffers; rkv_encoder_chunk_attn for the encoder; the same input
+pools), checked on sampled (layer, stream) outputs that the oracle computes
+one by one, plus properties that hold at any size (every plan bit-exact
+against the oracle schedule, all outputs finite)."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import attention as att
+from oracle import fp16 as of
 from oracle import schedule as sch
 from oracle import storage as stg
 from rolling_window_kv_amd import synth
@@ -26,8 +28,8 @@ def _history(pool_pair, steps):
     return tuple(f64(x)[idx] for x in (q, k, v))
 
 
-def _check_plans(rkv, cache, mode, windows, caps, origins, steps, dc=1, F=1):
-    got = cache.plan_host()
+def _check_plans(rkv, got, mode, windows, caps, origins, steps, dc=1, F=1):
+    """got: the plans (PLAN_DTYPE) of step steps - 1."""
     S = len(windows)
     for s in range(S):
         st = sch.init_state(mode, int(windows[s]), int(caps[s]), int(origins[s]), dc, F)
@@ -38,42 +40,50 @@ def _check_plans(rkv, cache, mode, windows, caps, origins, steps, dc=1, F=1):
             assert int(got[f][s]) == getattr(ref, f), (s, f)
 
 
-def _run_decoder_fused(rkv, cfg, slots, windows, caps, origins, q, k, v, steps, keep=()):
+def _run_decoder_bench(rkv, cfg, slots, windows, caps, origins, q, k, v, steps, keep=()):
+    """The bench's step: rkv_advance primes the first plan, then one pipelined
+    launch per step (after rkv_compact in compaction mode).  Returns the
+    cache, the last output, kept outputs and the last step's plans."""
     dev = q.device
     P = q.shape[0]
     cache = rkv.Cache(cfg, slots, windows, caps, origins, device=dev, zero=False)
     out = torch.empty(q.shape[1:], dtype=torch.bfloat16, device=dev)
+    plans = [cache.plan, cache.plan_next]
+    rkv.rkv_advance(cfg, cache.state, plans[0])
     kept = {}
     for t in range(steps):
-        rkv.rkv_advance(cfg, cache.state, cache.plan)
+        cur, nxt = plans[t % 2], plans[(t + 1) % 2]
         if cfg.mode == rkv.RKV_MODE_COMPACT:
-            rkv.rkv_compact(cfg, cache.plan, cache.kv)
-        rkv.rkv_decode_step(cfg, cache.plan, cache.kv, q[t % P], k[t % P], v[t % P], out,
-                            cache.workspace)
+            rkv.rkv_compact(cfg, cur, cache.kv)
+        rkv.rkv_decode_step_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[t % P], k[t % P],
+                                      v[t % P], out, cache.workspace)
         if t in keep:
             kept[t] = out.clone()
     torch.cuda.synchronize()
-    return cache, out, kept
+    last = plans[(steps - 1) % 2].cpu().numpy().view(rkv.PLAN_DTYPE)
+    return cache, out, kept, last
 
 
-def test_decode_36_layers_64_streams_w375():
+@pytest.mark.parametrize("fp16", [False, True])
+def test_decode_36_layers_64_streams_w375(fp16):
     rkv = rkv_mod()
     dev = device()
     L, S, W, dc, P, seed = 36, 64, 375, 25, 64, 1002
     steps = 450                                         # fills, then re-bases at 399, 424, 449
     q, k, v = synth.decoder_pool(seed, L, S, P, HQ, HKV, D)
-    cfg = rkv.make_cfg(S, L, rebase_chunk=dc)
-    say("case: 36x64 W=375 dc=25, 450 steps fused")
-    cache, out, kept = _run_decoder_fused(rkv, cfg, W, W, W, 0, q.to(dev), k.to(dev), v.to(dev),
-                                          steps, keep=(420,))
+    cfg = rkv.make_cfg(S, L, rebase_chunk=dc, flags=rkv.RKV_F_KV_FP16 if fp16 else 0)
+    say(f"case: 36x64 W=375 dc=25, 450 pipelined steps, fp16 cache {fp16}")
+    cache, out, kept, last = _run_decoder_bench(rkv, cfg, W, W, W, 0, q.to(dev), k.to(dev),
+                                                v.to(dev), steps, keep=(420,))
     assert torch.isfinite(out.float()).all()
-    _check_plans(rkv, cache, sch.MODE_REBASE, [W] * S, [W] * S, [0] * S, steps, dc)
+    _check_plans(rkv, last, sch.MODE_REBASE, [W] * S, [W] * S, [0] * S, steps, dc)
     got = {449: f64(out), 420: f64(kept[420])}
     for (l, s) in [(0, 0), (35, 63), (17, 5), (3, 40), (29, 22)]:
         pair = synth.decoder_pair(seed, l, s, P, HQ, HKV, D)
         qh, kh, vh = _history(pair, steps)
         exact = att.window_decode(qh, kh, vh, W, 1e6, steps=[420, 449])
-        ring = stg.RebaseRing(HQ, HKV, D, W, dc, 1e6)
+        ring = stg.RebaseRing(HQ, HKV, D, W, dc, 1e6,
+                              rounder=of.round_f16 if fp16 else stg.round_bf16)
         sf = {t: ring.step(qh[t], kh[t], vh[t])[1] for t in range(steps)}
         for t in (420, 449):
             check_close(got[t][l, s], exact[t], 2e-2, f"36x64 l{l} s{s} t{t} vs exact")
@@ -92,10 +102,10 @@ def test_decode_mixed_clocks_256_streams_outliers():
     q, k, v = synth.decoder_pool(seed, L, S, P, HQ, HKV, D, 0.01)
     cfg = rkv.make_cfg(S, L, rebase_chunk=dc)
     say("case: 36x256 mixed W, offsets, outliers")
-    cache, out, _ = _run_decoder_fused(rkv, cfg, 375, windows, windows, origins, q.to(dev),
-                                       k.to(dev), v.to(dev), steps)
+    cache, out, _, last = _run_decoder_bench(rkv, cfg, 375, windows, windows, origins,
+                                             q.to(dev), k.to(dev), v.to(dev), steps)
     assert torch.isfinite(out.float()).all()
-    _check_plans(rkv, cache, sch.MODE_REBASE, windows, windows, origins, steps, dc)
+    _check_plans(rkv, last, sch.MODE_REBASE, windows, windows, origins, steps, dc)
     got = f64(out)
     T = steps - 1
     for (l, s) in [(0, 0), (20, 85), (35, 86), (7, 170), (30, 171), (11, 255)]:
@@ -120,10 +130,10 @@ def test_compaction_26_layers_16_streams_w8192():
     q, k, v = synth.decoder_pool(seed, L, S, P, HQ, HKV, D)
     cfg = rkv.make_cfg(S, L, mode=rkv.RKV_MODE_COMPACT)
     say("case: 26x16 W=8192 cap=9216 compaction")
-    cache, out, _ = _run_decoder_fused(rkv, cfg, cap, W, cap, 0, q.to(dev), k.to(dev), v.to(dev),
-                                       steps)
+    cache, out, _, last = _run_decoder_bench(rkv, cfg, cap, W, cap, 0, q.to(dev), k.to(dev),
+                                             v.to(dev), steps)
     assert torch.isfinite(out.float()).all()
-    _check_plans(rkv, cache, sch.MODE_COMPACT, [W] * S, [cap] * S, [0] * S, steps)
+    _check_plans(rkv, last, sch.MODE_COMPACT, [W] * S, [cap] * S, [0] * S, steps)
     got = f64(out)
     T = steps - 1
     for (l, s) in [(0, 0), (25, 15), (13, 7)]:
@@ -152,7 +162,7 @@ def test_encoder_32_layers_128_streams():
                                    out, cache.workspace)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    _check_plans(rkv, cache, sch.MODE_ENC, [W] * S, [cap] * S, [0] * S, steps, 1, F)
+    _check_plans(rkv, cache.plan_host(), sch.MODE_ENC, [W] * S, [cap] * S, [0] * S, steps, 1, F)
     got = f64(out)
     for (l, s) in [(0, 0), (31, 127), (16, 64)]:
         pair = synth.encoder_pair(seed, l, s, P, F, H, d)
