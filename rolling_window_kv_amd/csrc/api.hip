@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "rkv_internal.h"
+#include "rkv_mel.h"
 
 namespace {
 

@@ -18,6 +18,7 @@
 
 #include "rkv_device.h"
 #include "rkv_internal.h"
+#include "rkv_mel.h"
 
 namespace rkv {
 namespace {

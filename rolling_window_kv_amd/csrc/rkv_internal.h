@@ -56,9 +56,6 @@ struct ResetList {
   int32_t stream[kMax];
   int64_t origin[kMax];
 };
-hipError_t launch_mel(const rkv_mel_cfg* c, const float* tail_in, float* tail_out,
-                      const float* samples, const float* filters, float* out,
-                      hipStream_t stream);
 hipError_t launch_reset(const rkv_cfg* cfg, rkv_stream_state* st, rkv_step_plan* plan,
                         const ResetList& list, hipStream_t stream);
 hipError_t launch_append(const rkv_cfg* cfg, const rkv_step_plan* plan, const RingArgs& ring,
