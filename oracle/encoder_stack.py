@@ -1,0 +1,63 @@
+"""Incremental encoder step through a stack of layers (oracle).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): float64 NumPy.
+
+voxtral.c explainer, section 三: the causal audio encoder (32 layers; the
+Audio8 explainer's table: hidden 1280, a 750-frame sliding window) encodes
+only the new positions of each step, each layer attending from the new
+frames to its cached K/V.  This runs that step through every layer with the
+chunk attention of :class:`oracle.storage.EncoderRing` (K rotated at its
+logical position and rounded to bfloat16 when stored).
+
+Readings taken where the pages give no detail of the layer: a pre-norm
+residual layer, x += Wo attn(RMSNorm(x) Wq, Wk, Wv); x += W2 gelu(W1
+RMSNorm(x)), with RMSNorm(x) = x / sqrt(mean(x^2) + eps) * g, the exact
+(erf) GELU, an MLP of 4 x hidden, no biases; 20 heads of 64 as the encoder's
+chosen split.  Storage-faithful points (as the GPU stores them): the normed
+activations, q, k, v, the attention output and the MLP activation are
+bfloat16; the residual stream stays in full precision (float32 on the GPU).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import storage
+from .bf16 import round_bf16
+
+
+def rmsnorm(x, g, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def gelu(x):
+    x = np.asarray(x, np.float64)
+    return 0.5 * x * (1.0 + np.vectorize(math.erf)(x / math.sqrt(2.0)))
+
+
+class EncoderStack:
+    """One stream's encoder layers, stepped F frames at a time."""
+
+    def __init__(self, weights, heads, d, window, frames, base, eps, origin=0,
+                 rounder=round_bf16):
+        self.w = [{n: np.asarray(t, np.float64) for n, t in lw.items()} for lw in weights]
+        self.h, self.d, self.f, self.eps = heads, d, frames, eps
+        self.r = rounder or (lambda x: np.asarray(x, np.float64))
+        self.rings = [storage.EncoderRing(heads, d, window, frames, base, origin,
+                                          rounder=rounder) for _ in weights]
+
+    def step(self, x):
+        """x [F, hidden] (the residual stream entering layer 0) -> after the last layer."""
+        x = np.asarray(x, np.float64)
+        r, F, H, d = self.r, self.f, self.h, self.d
+        for w, ring in zip(self.w, self.rings):
+            a = r(rmsnorm(x, w["g1"], self.eps))
+            q, k, v = (r(a @ w[n].T).reshape(F, H, d) for n in ("wq", "wk", "wv"))
+            _, att = ring.step(q, k, v)
+            x = x + r(att).reshape(F, H * d) @ w["wo"].T
+            a2 = r(rmsnorm(x, w["g2"], self.eps))
+            u = r(gelu(a2 @ w["w1"].T))
+            x = x + u @ w["w2"].T
+        return x

@@ -74,3 +74,35 @@ def start_offsets(seed, streams, high):
     """Per-stream start offsets, uniform integers in [0, high]."""
     rng = np.random.default_rng([int(seed), 0x5EED])
     return rng.integers(0, high + 1, size=streams).astype(np.int64)
+
+
+def encoder_stack_weights(seed, layers, hidden, ffn):
+    """Synthetic weights of a stack of pre-norm encoder layers (CPU bf16).
+
+    Per layer a dict: g1, g2 [hidden] = 1 + 0.1 N(0, 1); wq, wk, wv, wo
+    [hidden, hidden] and w1 [ffn, hidden], w2 [hidden, ffn] = N(0, 1) /
+    sqrt(fan_in) (row = output feature).  Layer l draws from [seed, l, -1].
+    """
+    out = []
+    for l in range(layers):
+        rng = np.random.default_rng([int(seed), int(l), 2 ** 31 - 1])
+
+        def mat(rows, cols):
+            x = rng.standard_normal((rows, cols), dtype=np.float32) / np.float32(np.sqrt(cols))
+            return torch.from_numpy(x).to(torch.bfloat16)
+
+        def gain():
+            x = 1.0 + 0.1 * rng.standard_normal(hidden, dtype=np.float32)
+            return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+
+        out.append(dict(g1=gain(), wq=mat(hidden, hidden), wk=mat(hidden, hidden),
+                        wv=mat(hidden, hidden), wo=mat(hidden, hidden), g2=gain(),
+                        w1=mat(ffn, hidden), w2=mat(hidden, ffn)))
+    return out
+
+
+def encoder_stack_inputs(seed, streams, period, frames, hidden):
+    """Frame embeddings entering the stack: [period, S, F, hidden] float32 N(0, 1)."""
+    rng = np.random.default_rng([int(seed), 2 ** 31 - 2])
+    return torch.from_numpy(rng.standard_normal((period, streams, frames, hidden),
+                                                dtype=np.float32))
