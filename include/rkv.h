@@ -394,6 +394,52 @@ int rkv_mel_step(const rkv_mel_cfg* cfg, const float* d_tail_in, float* d_tail_o
                  const float* d_samples, const float* d_filters, float* d_out,
                  void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Incremental encoder step through a stack of layers (voxtral.c explainer,
+ * section 三: the causal encoder computes only the new positions of a step,
+ * each layer attending from them to its cached K/V).  Every layer is a
+ * pre-norm residual block around the chunk attention:
+ *   a = RMSNorm(x) g1;  x += Wo attn(a Wq^T, a Wk^T, a Wv^T);
+ *   x += W2 gelu(W1 (RMSNorm(x) g2))
+ * (RMSNorm(x) = x / sqrt(mean(x^2) + eps), exact erf GELU, no biases), with
+ * the residual stream in float32 and the other activations in bfloat16.  The
+ * layer structure beyond the attention is not given by the sources; the
+ * synthetic weights make it a workload around the cache, not a model.
+ * ------------------------------------------------------------------------- */
+
+typedef struct rkv_encoder_cfg {
+  int32_t ffn;        /* MLP width, a multiple of 32 (4 x hidden) */
+  float norm_eps;     /* RMSNorm epsilon, >= 0 */
+  int32_t reserved[2];
+} rkv_encoder_cfg;
+
+/* Bytes of one layer's bfloat16 weights; a stack is num_layers of them back to
+ * back.  Per layer, in order: g1[hidden], wq, wk, wv, wo [hidden][hidden],
+ * g2[hidden], w1[ffn][hidden], w2[hidden][ffn], each matrix with one row per
+ * output feature; hidden = num_q_heads * head_dim.  0 on a bad cfg. */
+size_t rkv_encoder_layer_weight_bytes(const rkv_cfg* cfg, const rkv_encoder_cfg* ec);
+
+/* Workspace bytes of rkv_encoder_step for a cache of `slots` rows per head:
+ * bfloat16 a, q, k, v, att [S*F][hidden] and u [S*F][ffn], plus the chunk
+ * attention's workspace for one layer.  0 on a bad cfg. */
+size_t rkv_encoder_step_workspace_bytes(const rkv_cfg* cfg, const rkv_encoder_cfg* ec,
+                                        int32_t slots);
+
+/* One clock step of cfg->num_layers encoder layers for every stream (ENC_CHUNK
+ * mode, after rkv_advance: the plan is shared by all layers).  d_x [S][F][hidden]
+ * float32 (device) holds the F new frames' embeddings on entry and the stack's
+ * output on return.  Layer l reads weights at d_weights + l *
+ * rkv_encoder_layer_weight_bytes() and appends to, and attends over, the
+ * layer-l slice of the cache (kv->k + l * layer_stride, ...).  The launches
+ * are asynchronous on hip_stream; no allocation.  Errors as for
+ * rkv_encoder_chunk_attn, plus RKV_EINVAL for hidden or ffn not a multiple of
+ * 32 or a mode other than ENC_CHUNK, RKV_EUNSUPPORTED for RKV_F_OUT_F32,
+ * RKV_ESPACE for a short workspace and RKV_EALIGN for d_x, d_weights or
+ * the workspace not 16-byte aligned. */
+int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_step_plan* d_plan,
+                     const rkv_kv_view* kv, const void* d_weights, float* d_x,
+                     void* d_workspace, size_t workspace_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "rkv_internal.h"
+#include "rkv_encoder.h"
 #include "rkv_mel.h"
 
 namespace {
@@ -385,6 +386,112 @@ int rkv_decode_step_pipelined(const rkv_cfg* cfg, rkv_stream_state* d_state,
                               size_t workspace_bytes, void* hip_stream) {
   return attention(cfg, rkv::kDecodeFused, d_plan, kv, q, k_new, v_new, out, workspace,
                    workspace_bytes, hip_stream, d_state, d_plan_next);
+}
+
+static int check_encoder(const rkv_cfg* cfg, const rkv_encoder_cfg* ec) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!ec || cfg->mode != RKV_MODE_ENC_CHUNK) return RKV_EINVAL;
+  // the attention output is a bfloat16 activation of the stack
+  if (cfg->flags & RKV_F_OUT_F32) return RKV_EUNSUPPORTED;
+  const int hidden = cfg->num_q_heads * cfg->head_dim;
+  if (hidden % 32 || ec->ffn < 32 || ec->ffn % 32) return RKV_EINVAL;
+  if (!(ec->norm_eps >= 0.0f) || !isfinite(ec->norm_eps)) return RKV_EINVAL;
+  return RKV_OK;
+}
+
+static size_t encoder_layer_elems(const rkv_cfg* cfg, const rkv_encoder_cfg* ec) {
+  const size_t h = (size_t)cfg->num_q_heads * cfg->head_dim, f = (size_t)ec->ffn;
+  return 2 * h + 4 * h * h + 2 * h * f;
+}
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t rkv_encoder_layer_weight_bytes(const rkv_cfg* cfg, const rkv_encoder_cfg* ec) {
+  if (check_encoder(cfg, ec)) return 0;
+  return 2 * encoder_layer_elems(cfg, ec);
+}
+
+size_t rkv_encoder_step_workspace_bytes(const rkv_cfg* cfg, const rkv_encoder_cfg* ec,
+                                        int32_t slots) {
+  if (check_encoder(cfg, ec) || slots < 1) return 0;
+  const size_t tokens = (size_t)cfg->num_streams * cfg->new_rows;
+  const size_t h = (size_t)cfg->num_q_heads * cfg->head_dim;
+  rkv_cfg one = *cfg;
+  one.num_layers = 1;
+  return 5 * align256(2 * tokens * h) + align256(2 * tokens * ec->ffn) +
+         align256(workspace_for(&one, slots));
+}
+
+int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_step_plan* d_plan,
+                     const rkv_kv_view* kv, const void* d_weights, float* d_x,
+                     void* d_workspace, size_t workspace_bytes, void* hip_stream) {
+  int rc = check_encoder(cfg, ec);
+  if (rc) return rc;
+  if ((rc = check_kv(cfg, kv))) return rc;
+  if (!d_plan || !d_weights || !d_x || !d_workspace) return RKV_EINVAL;
+  if (!aligned16(d_weights) || !aligned16(d_x) || !aligned16(d_workspace)) return RKV_EALIGN;
+  const size_t need = rkv_encoder_step_workspace_bytes(cfg, ec, kv->slots);
+  if (workspace_bytes < need) return RKV_ESPACE;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const int M = cfg->num_streams * cfg->new_rows;
+  const int H = cfg->num_q_heads * cfg->head_dim, FF = ec->ffn;
+  // workspace carving
+  char* p = static_cast<char*>(d_workspace);
+  const size_t act = align256((size_t)2 * M * H);
+  uint16_t* a = reinterpret_cast<uint16_t*>(p);
+  uint16_t* q = reinterpret_cast<uint16_t*>(p + act);
+  uint16_t* k = reinterpret_cast<uint16_t*>(p + 2 * act);
+  uint16_t* v = reinterpret_cast<uint16_t*>(p + 3 * act);
+  uint16_t* att = reinterpret_cast<uint16_t*>(p + 4 * act);
+  uint16_t* u = reinterpret_cast<uint16_t*>(p + 5 * act);
+  void* aws = p + 5 * act + align256((size_t)2 * M * FF);
+  rkv_cfg one = *cfg;
+  one.num_layers = 1;
+  const size_t aws_bytes = workspace_bytes - (5 * act + align256((size_t)2 * M * FF));
+  const size_t layer_elems = encoder_layer_elems(cfg, ec);
+  hipError_t e;
+  for (int l = 0; l < cfg->num_layers; ++l) {
+    const uint16_t* w = static_cast<const uint16_t*>(d_weights) + (size_t)l * layer_elems;
+    const uint16_t* g1 = w;
+    const uint16_t* wq = g1 + H;
+    const uint16_t* wk = wq + (size_t)H * H;
+    const uint16_t* wv = wk + (size_t)H * H;
+    const uint16_t* wo = wv + (size_t)H * H;
+    const uint16_t* g2 = wo + (size_t)H * H;
+    const uint16_t* w1 = g2 + H;
+    const uint16_t* w2 = w1 + (size_t)FF * H;
+    if ((e = rkv::launch_rmsnorm(d_x, g1, a, M, H, ec->norm_eps, stream)) != hipSuccess)
+      return hip_status(e);
+    const uint16_t* wqkv[3] = {wq, wk, wv};
+    void* cqkv[3] = {q, k, v};
+    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kStoreBf16, wqkv, cqkv, 3, a, M, H, H,
+                              stream)) != hipSuccess)
+      return hip_status(e);
+    rkv_kv_view lv = *kv;
+    lv.k = static_cast<uint16_t*>(kv->k) + (size_t)l * kv->layer_stride;
+    lv.v = static_cast<uint16_t*>(kv->v) + (size_t)l * kv->layer_stride;
+    if ((rc = attention(&one, rkv::kEncoderFused, d_plan, &lv, q, k, v, att, aws, aws_bytes,
+                        hip_stream)))
+      return rc;
+    const uint16_t* wos[1] = {wo};
+    void* xs[1] = {d_x};
+    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kAddF32, wos, xs, 1, att, M, H, H, stream)) !=
+        hipSuccess)
+      return hip_status(e);
+    if ((e = rkv::launch_rmsnorm(d_x, g2, a, M, H, ec->norm_eps, stream)) != hipSuccess)
+      return hip_status(e);
+    const uint16_t* w1s[1] = {w1};
+    void* us[1] = {u};
+    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kGeluBf16, w1s, us, 1, a, M, FF, H, stream)) !=
+        hipSuccess)
+      return hip_status(e);
+    const uint16_t* w2s[1] = {w2};
+    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kAddF32, w2s, xs, 1, u, M, H, FF, stream)) !=
+        hipSuccess)
+      return hip_status(e);
+  }
+  return RKV_OK;
 }
 
 int rkv_encoder_chunk_attn(const rkv_cfg* cfg, const rkv_step_plan* d_plan,

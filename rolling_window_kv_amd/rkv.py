@@ -42,6 +42,7 @@ ENTRY_POINTS = (
     "rkv_decode_step_pipelined",
     "rkv_encoder_chunk_attn", "rkv_reset_streams", "rkv_restart_step",
     "rkv_mel_filters_host", "rkv_mel_step",
+    "rkv_encoder_layer_weight_bytes", "rkv_encoder_step_workspace_bytes", "rkv_encoder_step",
 )
 
 RKV_STREAM_MAX_DECODE_KV = 2000
@@ -80,6 +81,11 @@ class rkv_kv_view(ctypes.Structure):
         ("head_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
         ("slots", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
+
+
+class rkv_encoder_cfg(ctypes.Structure):
+    _fields_ = [("ffn", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class rkv_mel_cfg(ctypes.Structure):
@@ -154,6 +160,10 @@ def lib():
                                      ctypes.c_int),
             "rkv_mel_step": ([ctypes.POINTER(rkv_mel_cfg), vp, vp, vp, vp, vp, vp],
                              ctypes.c_int),
+            "rkv_encoder_layer_weight_bytes": ([pc, ctypes.POINTER(rkv_encoder_cfg)], sz),
+            "rkv_encoder_step_workspace_bytes": ([pc, ctypes.POINTER(rkv_encoder_cfg), i32], sz),
+            "rkv_encoder_step": ([pc, ctypes.POINTER(rkv_encoder_cfg), vp, pk, vp, vp, vp, sz, vp],
+                                 ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -293,6 +303,37 @@ def rkv_restart_step(cfg, state, tokens):
     if n < 0:
         raise RkvError("rkv_restart_step", n)
     return restart[:n].copy(), reason
+
+
+def make_encoder_cfg(ffn=5120, norm_eps=1e-5) -> rkv_encoder_cfg:
+    return rkv_encoder_cfg(ffn, norm_eps, (ctypes.c_int32 * 2)(0, 0))
+
+
+ENCODER_WEIGHT_ORDER = ("g1", "wq", "wk", "wv", "wo", "g2", "w1", "w2")
+
+
+def pack_encoder_weights(layers):
+    """Per-layer dicts of bfloat16 tensors -> one contiguous bfloat16 tensor in
+    the library's layer layout (include/rkv.h, rkv_encoder_layer_weight_bytes)."""
+    import torch
+    return torch.cat([lw[n].reshape(-1) for lw in layers for n in ENCODER_WEIGHT_ORDER])
+
+
+def rkv_encoder_layer_weight_bytes(cfg, ecfg) -> int:
+    return int(lib().rkv_encoder_layer_weight_bytes(ctypes.byref(cfg), ctypes.byref(ecfg)))
+
+
+def rkv_encoder_step_workspace_bytes(cfg, ecfg, slots) -> int:
+    return int(lib().rkv_encoder_step_workspace_bytes(ctypes.byref(cfg), ctypes.byref(ecfg),
+                                                      int(slots)))
+
+
+def rkv_encoder_step(cfg, ecfg, plan, kv, weights, x, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("rkv_encoder_step",
+           lib().rkv_encoder_step(ctypes.byref(cfg), ctypes.byref(ecfg), _ptr(plan),
+                                  ctypes.byref(kv), _ptr(weights), _ptr(x), _ptr(workspace),
+                                  nbytes, _stream(stream)))
 
 
 def make_mel_cfg(num_streams, n_fft=400, hop=160, n_mels=128,

@@ -253,3 +253,42 @@ def test_fp16_cache_flag(rkv):
     assert rkv.lib().rkv_validate_cfg(ctypes.byref(enc)) == rkv.RKV_EUNSUPPORTED
     unknown = good_cfg(rkv, flags=1 << 3)
     assert rkv.lib().rkv_validate_cfg(ctypes.byref(unknown)) == rkv.RKV_EUNSUPPORTED
+
+
+def test_encoder_step_sizes_and_validation(rkv):
+    S, L, H, d, F, slots, ffn = 2, 3, 4, 64, 4, 24, 1024
+    hidden = H * d
+    cfg = rkv.make_cfg(S, L, num_q_heads=H, num_kv_heads=H, head_dim=d,
+                       mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F)
+    ec = rkv.make_encoder_cfg(ffn=ffn, norm_eps=1e-5)
+    # g1, wq, wk, wv, wo, g2, w1, w2 in bfloat16
+    assert rkv.rkv_encoder_layer_weight_bytes(cfg, ec) == 2 * (2 * hidden + 4 * hidden ** 2
+                                                                + 2 * hidden * ffn)
+    ws = rkv.rkv_encoder_step_workspace_bytes(cfg, ec, slots)
+    assert ws >= 2 * S * F * (5 * hidden + ffn)
+    bad = [rkv.make_encoder_cfg(ffn=48), rkv.make_encoder_cfg(ffn=0),
+           rkv.make_encoder_cfg(norm_eps=-1.0), rkv.make_encoder_cfg(norm_eps=float("nan"))]
+    for b in bad:
+        assert rkv.rkv_encoder_layer_weight_bytes(cfg, b) == 0
+        assert rkv.rkv_encoder_step_workspace_bytes(cfg, b, slots) == 0
+    dec = good_cfg(rkv)
+    assert rkv.rkv_encoder_layer_weight_bytes(dec, ec) == 0
+    assert rkv.rkv_encoder_step_workspace_bytes(cfg, ec, 0) == 0
+    kv = rkv.rkv_kv_view(FAKE, FAKE + 0x1000000, None, S * H * slots * d, H * slots * d,
+                         slots * d, d, slots, 0)
+    c, e, k = ctypes.byref(cfg), ctypes.byref(ec), ctypes.byref(kv)
+    P, W, X, WS = (ctypes.c_void_p(FAKE + o) for o in (0x2000000, 0x3000000, 0x4000000,
+                                                       0x5000000))
+    N = None
+    step = lambda *a: call(rkv, "rkv_encoder_step", *a)
+    assert step(c, e, N, k, W, X, WS, ws, N) == rkv.RKV_EINVAL
+    assert step(c, None, P, k, W, X, WS, ws, N) == rkv.RKV_EINVAL
+    assert step(c, e, P, k, W, ctypes.c_void_p(FAKE + 0x4000008), WS, ws, N) == rkv.RKV_EALIGN
+    assert step(c, e, P, k, ctypes.c_void_p(FAKE + 0x3000004), X, WS, ws, N) == rkv.RKV_EALIGN
+    assert step(c, e, P, k, W, X, WS, ws - 1, N) == rkv.RKV_ESPACE
+    f32 = rkv.make_cfg(S, L, num_q_heads=H, num_kv_heads=H, head_dim=d,
+                       mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F, flags=rkv.RKV_F_OUT_F32)
+    assert step(ctypes.byref(f32), e, P, k, W, X, WS, ws, N) == rkv.RKV_EUNSUPPORTED
+    assert step(ctypes.byref(dec), e, P, k, W, X, WS, ws, N) == rkv.RKV_EINVAL
+    assert step(c, ctypes.byref(bad[0]), P, k, W, X, WS, ws, N) == rkv.RKV_EINVAL
+    assert rkv.rkv_last_hip_error() == 0

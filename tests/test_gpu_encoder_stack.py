@@ -1,0 +1,119 @@
+"""rkv_encoder_step (the incremental encoder step through a stack of layers
+around the chunk attention) against the float64 oracle with bfloat16 storage
+points (oracle.encoder_stack).
+
+Two gates:
+
+* a small stack run end to end over enough steps to wrap the ring, with a
+  ragged token count, against the oracle stack;
+* the full 32-layer, 128-stream, hidden 1280 shape layer by layer: every
+  layer's GPU output is compared with the oracle layer fed the GPU's own
+  input of that layer (and its own ring of K/V built from those inputs), and
+  the one 32-layer call is checked to equal the 32 one-layer calls bit for
+  bit.  End to end, a 1-ulp bfloat16 rounding flip in a stored activation of
+  one layer feeds every later layer, so the difference to the oracle stack
+  grows with depth without any arithmetic being wrong (2.0e-2 at 32 layers
+  against 0.3e-2 per layer); that figure is reported, and gated only by the
+  layer count times the per-layer gate."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import encoder_stack as oes
+from rolling_window_kv_amd import synth
+
+from gpu_util import device, rkv_mod, say
+
+pytestmark = pytest.mark.gpu
+
+GATE = 2e-2          # max |gpu - oracle| / max(1, rms(oracle)) of a layer's output
+
+
+def _err(got, want):
+    return float(np.abs(got - want).max() / max(1.0, np.sqrt((want ** 2).mean())))
+
+
+def _setup(rkv, L, S, H, d, F, W, ffn, seed, steps):
+    dev = device()
+    hidden = H * d
+    ecfg = rkv.make_encoder_cfg(ffn=ffn, norm_eps=1e-5)
+    layers = synth.encoder_stack_weights(seed, L, hidden, ffn)
+    xin = synth.encoder_stack_inputs(seed, S, steps, F, hidden)
+    wts = [{n: t.float().numpy() for n, t in lw.items()} for lw in layers]
+    return dev, ecfg, layers, xin, wts
+
+
+def _cfg(rkv, L, S, H, d, F):
+    return rkv.make_cfg(S, L, num_q_heads=H, num_kv_heads=H, head_dim=d,
+                        mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F)
+
+
+def test_small_stack_wraps_the_ring():
+    """3 layers, 3 streams x 4 frames = 12 tokens (a ragged tile), hidden 256,
+    window 20 frames in a 24-slot ring: 12 steps wrap it twice."""
+    rkv = rkv_mod()
+    L, S, H, d, F, W, ffn, steps = 3, 3, 4, 64, 4, 20, 1024, 12
+    dev, ecfg, layers, xin, wts = _setup(rkv, L, S, H, d, F, W, ffn, 77, steps)
+    cfg = _cfg(rkv, L, S, H, d, F)
+    cap = W + F
+    cache = rkv.Cache(cfg, cap, W, cap, 0, device=dev)
+    wdev = rkv.pack_encoder_weights(layers).to(dev)
+    assert wdev.numel() * 2 == L * rkv.rkv_encoder_layer_weight_bytes(cfg, ecfg)
+    ws = torch.empty(rkv.rkv_encoder_step_workspace_bytes(cfg, ecfg, cap), dtype=torch.uint8,
+                     device=dev)
+    outs = []
+    for t in range(steps):
+        x = xin[t].to(dev).contiguous()
+        rkv.rkv_advance(cfg, cache.state, cache.plan)
+        rkv.rkv_encoder_step(cfg, ecfg, cache.plan, cache.kv, wdev, x, ws)
+        outs.append(x.cpu().numpy().astype(np.float64))
+    worst = 0.0
+    for s in range(S):
+        ref = oes.EncoderStack(wts, H, d, W, F, 1e6, 1e-5)
+        for t in range(steps):
+            worst = max(worst, _err(outs[t][s], ref.step(xin[t, s].numpy().astype(np.float64))))
+    say(f"small stack: max |gpu - oracle| / max(1, rms) = {worst:.3e}")
+    assert worst < GATE
+
+
+def test_full_shape_32_layers_128_streams():
+    rkv = rkv_mod()
+    L, S, H, d, F, W, ffn, steps = 32, 128, 20, 64, 4, 750, 5120, 3
+    check = (0, 77, 127)
+    dev, ecfg, layers, xin, wts = _setup(rkv, L, S, H, d, F, W, ffn, 78, steps)
+    cap = W + F
+    cfg = _cfg(rkv, L, S, H, d, F)
+    cfg1 = _cfg(rkv, 1, S, H, d, F)
+    fused = rkv.Cache(cfg, cap, W, cap, 0, device=dev)
+    per = [rkv.Cache(cfg1, cap, W, cap, 0, device=dev) for _ in range(L)]
+    wdev = rkv.pack_encoder_weights(layers).to(dev)
+    lw = rkv.rkv_encoder_layer_weight_bytes(cfg, ecfg) // 2
+    assert wdev.numel() == L * lw
+    ws = torch.empty(rkv.rkv_encoder_step_workspace_bytes(cfg, ecfg, cap), dtype=torch.uint8,
+                     device=dev)
+    oracle_layers = {s: [oes.EncoderStack([w], H, d, W, F, 1e6, 1e-5) for w in wts]
+                     for s in check}
+    oracle_stack = {s: oes.EncoderStack(wts, H, d, W, F, 1e6, 1e-5) for s in check}
+    worst_layer, worst_end = 0.0, 0.0
+    for t in range(steps):
+        xf = xin[t].to(dev).contiguous()
+        rkv.rkv_advance(cfg, fused.state, fused.plan)
+        rkv.rkv_encoder_step(cfg, ecfg, fused.plan, fused.kv, wdev, xf, ws)
+        xl = xin[t].to(dev).contiguous()
+        trace = [xl[:, :, :].cpu()]
+        for l, c in enumerate(per):
+            rkv.rkv_advance(cfg1, c.state, c.plan)
+            rkv.rkv_encoder_step(cfg1, ecfg, c.plan, c.kv, wdev[l * lw:(l + 1) * lw], xl, ws)
+            trace.append(xl[:, :, :].cpu())
+        assert torch.equal(xf.cpu(), trace[-1]), f"step {t}: 32-layer call != 32 one-layer calls"
+        for s in check:
+            for l in range(L):
+                got_in = trace[l][s].numpy().astype(np.float64)
+                want = oracle_layers[s][l].step(got_in)
+                worst_layer = max(worst_layer, _err(trace[l + 1][s].numpy().astype(np.float64),
+                                                    want))
+            want = oracle_stack[s].step(xin[t, s].numpy().astype(np.float64))
+            worst_end = max(worst_end, _err(trace[-1][s].numpy().astype(np.float64), want))
+        say(f"step {t}: worst layer {worst_layer:.3e}, end to end {worst_end:.3e}")
+    assert worst_layer < GATE
+    assert worst_end < L * GATE
