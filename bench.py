@@ -399,6 +399,79 @@ def run_mel(args):
             "cpu_baseline": None}
 
 
+def run_encoder_stack(args):
+    """The incremental encoder step through the whole stack (rkv_advance +
+    rkv_encoder_step): 32 layers, hidden 1280 (20 heads of 64), MLP 5120,
+    S streams x 4 new frames per 80 ms step, 750-frame window (filled by
+    untimed steps first); synthetic weights.  The step reads every layer's
+    cached window (K and V, 750 x 1280 bfloat16 per stream) and weights once,
+    so it is bound by HBM: reported against 8 TB/s with the algorithmic bytes
+    of a step (per layer the window read, the appended K/V rows and the
+    layer's weights; the float32 residual stream in and out once).  The matrix
+    flops (the six projections, 2 x tokens x (4 hidden^2 + 2 hidden ffn), and
+    the chunk attention, 4 x frames x (W + F) x hidden per stream) are
+    reported beside it: at 0.7 TFLOP per step they need an eighth of the time
+    the bytes do."""
+    import torch
+    from rolling_window_kv_amd import rkv, synth
+    S = args.encoder_stack
+    L, H, d, F, W, ffn = 32, 20, 64, 4, 750, 5120
+    hidden = H * d
+    steps = args.steps or 50
+    warm = args.warmup if args.warmup is not None else 5
+    dev = torch.device("cuda:0")
+    cfg = rkv.make_cfg(S, L, num_q_heads=H, num_kv_heads=H, head_dim=d,
+                       mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F)
+    ecfg = rkv.make_encoder_cfg(ffn=ffn, norm_eps=1e-5)
+    cap = W + F
+    cache = rkv.Cache(cfg, cap, W, cap, 0, device=dev)
+    wdev = rkv.pack_encoder_weights(synth.encoder_stack_weights(5, L, hidden, ffn)).to(dev)
+    ws = torch.empty(rkv.rkv_encoder_step_workspace_bytes(cfg, ecfg, cap), dtype=torch.uint8,
+                     device=dev)
+    P = 4
+    xin = synth.encoder_stack_inputs(5, S, P, F, hidden).to(dev)
+    x = torch.empty_like(xin[0])
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        x.copy_(xin[i % P])
+        rkv.rkv_advance(cfg, cache.state, cache.plan)
+        rkv.rkv_encoder_step(cfg, ecfg, cache.plan, cache.kv, wdev, x, ws)
+
+    prefill = (cap + F - 1) // F          # untimed: the window is full from then on
+    for i in range(prefill + warm):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        step(prefill + warm + i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    tokens = S * F
+    flops = L * (2.0 * tokens * (4 * hidden * hidden + 2 * hidden * ffn)
+                 + 4.0 * S * F * cap * hidden)
+    tflops = flops / (ms * 1e-3) / 1e12
+    row = hidden * 2
+    nbytes = (L * (S * (W * 2 * row + 2 * F * row)
+                   + rkv.rkv_encoder_layer_weight_bytes(cfg, ecfg)) + 2 * tokens * hidden * 4)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"metric": "encoder frames/s (32-layer incremental step)",
+            "value": round(tokens / ms * 1e3, 1), "unit": "frames/s", "n_gpus": 1,
+            "steps": steps, "warmup": warm, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"incremental encoder step: {L} layers, hidden {hidden} "
+                                   f"({H}x{d}), MLP {ffn}, {S} streams x {F} frames, "
+                                   f"window {W}; synthetic weights"},
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                         "kernel": "rkv_encoder_step (whole step)", "bytes_per_step": nbytes,
+                         "matrix_tflops": round(tflops, 2), "flops_per_step": flops},
+            "cpu_baseline": None}
+
+
 def summarize_rocprof(root, last=0):
     """Per-kernel figures from a rocprofv3 CSV output folder: its own --stats
     table, mean dispatch duration from the kernel trace (and, with last > 0,
@@ -465,6 +538,9 @@ def main():
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
     ap.add_argument("--mel", type=int, default=0, metavar="STREAMS",
                     help="time the rolling log-mel front end for STREAMS streams instead")
+    ap.add_argument("--encoder-stack", type=int, default=0, metavar="STREAMS",
+                    help="time the 32-layer incremental encoder step for STREAMS streams "
+                         "instead")
     ap.add_argument("--kv-fp16", action="store_true",
                     help="store K and V as fp16 (the fp16 cache variant; decoder workloads)")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
@@ -498,6 +574,9 @@ def main():
         sys.exit(2)
     if args.mel:
         print(json.dumps(run_mel(args)), flush=True)
+        return
+    if args.encoder_stack:
+        print(json.dumps(run_encoder_stack(args)), flush=True)
         return
     c = dict(CONFIGS[args.config])
     if args.kv_fp16 and c["mode"] == "enc":

@@ -408,7 +408,7 @@ int rkv_mel_step(const rkv_mel_cfg* cfg, const float* d_tail_in, float* d_tail_o
  * ------------------------------------------------------------------------- */
 
 typedef struct rkv_encoder_cfg {
-  int32_t ffn;        /* MLP width, a multiple of 32 (4 x hidden) */
+  int32_t ffn;        /* MLP width, a multiple of 64 (4 x hidden) */
   float norm_eps;     /* RMSNorm epsilon, >= 0 */
   int32_t reserved[2];
 } rkv_encoder_cfg;
@@ -420,8 +420,10 @@ typedef struct rkv_encoder_cfg {
 size_t rkv_encoder_layer_weight_bytes(const rkv_cfg* cfg, const rkv_encoder_cfg* ec);
 
 /* Workspace bytes of rkv_encoder_step for a cache of `slots` rows per head:
- * bfloat16 a, q, k, v, att [S*F][hidden] and u [S*F][ffn], plus the chunk
- * attention's workspace for one layer.  0 on a bad cfg. */
+ * bfloat16 a, q, k, v, att [S*F][hidden] and u [S*F][ffn], float32 partial
+ * sums [4][S*F][hidden] of the two products added into the residual stream
+ * (computed in k-slices, added in slice order), plus the chunk attention's
+ * workspace for one layer.  0 on a bad cfg. */
 size_t rkv_encoder_step_workspace_bytes(const rkv_cfg* cfg, const rkv_encoder_cfg* ec,
                                         int32_t slots);
 
@@ -433,7 +435,7 @@ size_t rkv_encoder_step_workspace_bytes(const rkv_cfg* cfg, const rkv_encoder_cf
  * layer-l slice of the cache (kv->k + l * layer_stride, ...).  The launches
  * are asynchronous on hip_stream; no allocation.  Errors as for
  * rkv_encoder_chunk_attn, plus RKV_EINVAL for hidden or ffn not a multiple of
- * 32 or a mode other than ENC_CHUNK, RKV_EUNSUPPORTED for RKV_F_OUT_F32,
+ * 64, hidden above 4096 or a mode other than ENC_CHUNK, RKV_EUNSUPPORTED for RKV_F_OUT_F32,
  * RKV_ESPACE for a short workspace and RKV_EALIGN for d_x, d_weights or
  * the workspace not 16-byte aligned. */
 int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_step_plan* d_plan,

@@ -395,7 +395,8 @@ static int check_encoder(const rkv_cfg* cfg, const rkv_encoder_cfg* ec) {
   // the attention output is a bfloat16 activation of the stack
   if (cfg->flags & RKV_F_OUT_F32) return RKV_EUNSUPPORTED;
   const int hidden = cfg->num_q_heads * cfg->head_dim;
-  if (hidden % 32 || ec->ffn < 32 || ec->ffn % 32) return RKV_EINVAL;
+  if (hidden % 64 || hidden > rkv::kEncoderMaxHidden || ec->ffn < 64 || ec->ffn % 64)
+    return RKV_EINVAL;
   if (!(ec->norm_eps >= 0.0f) || !isfinite(ec->norm_eps)) return RKV_EINVAL;
   return RKV_OK;
 }
@@ -412,6 +413,14 @@ size_t rkv_encoder_layer_weight_bytes(const rkv_cfg* cfg, const rkv_encoder_cfg*
   return 2 * encoder_layer_elems(cfg, ec);
 }
 
+// k-slices of the two products that add into the residual stream (the
+// output projection and the MLP's second product): their float32 partial
+// sums are added, in slice order, by the RMSNorm launch that reads x next.
+static int encoder_splits(int K) {
+  const int stages = K / 64;
+  return stages % 4 == 0 ? 4 : stages % 2 == 0 ? 2 : 1;
+}
+
 size_t rkv_encoder_step_workspace_bytes(const rkv_cfg* cfg, const rkv_encoder_cfg* ec,
                                         int32_t slots) {
   if (check_encoder(cfg, ec) || slots < 1) return 0;
@@ -420,7 +429,7 @@ size_t rkv_encoder_step_workspace_bytes(const rkv_cfg* cfg, const rkv_encoder_cf
   rkv_cfg one = *cfg;
   one.num_layers = 1;
   return 5 * align256(2 * tokens * h) + align256(2 * tokens * ec->ffn) +
-         align256(workspace_for(&one, slots));
+         align256(4 * rkv::kGemmMaxSet * tokens * h) + align256(workspace_for(&one, slots));
 }
 
 int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_step_plan* d_plan,
@@ -436,7 +445,9 @@ int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_st
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int M = cfg->num_streams * cfg->new_rows;
   const int H = cfg->num_q_heads * cfg->head_dim, FF = ec->ffn;
-  // workspace carving
+  const float eps = ec->norm_eps;
+  // workspace: bfloat16 a, q, k, v, att [M][H], u [M][FF]; float32 partial
+  // sums [kGemmMaxSet][M][H]; then the chunk attention's own workspace
   char* p = static_cast<char*>(d_workspace);
   const size_t act = align256((size_t)2 * M * H);
   uint16_t* a = reinterpret_cast<uint16_t*>(p);
@@ -445,12 +456,18 @@ int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_st
   uint16_t* v = reinterpret_cast<uint16_t*>(p + 3 * act);
   uint16_t* att = reinterpret_cast<uint16_t*>(p + 4 * act);
   uint16_t* u = reinterpret_cast<uint16_t*>(p + 5 * act);
-  void* aws = p + 5 * act + align256((size_t)2 * M * FF);
+  float* part = reinterpret_cast<float*>(p + 5 * act + align256((size_t)2 * M * FF));
+  const size_t head = 5 * act + align256((size_t)2 * M * FF) +
+                      align256((size_t)4 * rkv::kGemmMaxSet * M * H);
+  void* aws = p + head;
+  const size_t aws_bytes = workspace_bytes - head;
+  const int64_t part_stride = (int64_t)M * H;
   rkv_cfg one = *cfg;
   one.num_layers = 1;
-  const size_t aws_bytes = workspace_bytes - (5 * act + align256((size_t)2 * M * FF));
   const size_t layer_elems = encoder_layer_elems(cfg, ec);
+  const int so = encoder_splits(H), s2 = encoder_splits(FF);
   hipError_t e;
+  int pending = 0;            // partial sums of the previous product not yet in x
   for (int l = 0; l < cfg->num_layers; ++l) {
     const uint16_t* w = static_cast<const uint16_t*>(d_weights) + (size_t)l * layer_elems;
     const uint16_t* g1 = w;
@@ -461,11 +478,14 @@ int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_st
     const uint16_t* g2 = wo + (size_t)H * H;
     const uint16_t* w1 = g2 + H;
     const uint16_t* w2 = w1 + (size_t)FF * H;
-    if ((e = rkv::launch_rmsnorm(d_x, g1, a, M, H, ec->norm_eps, stream)) != hipSuccess)
+    // x += previous layer's MLP output; a = RMSNorm(x) g1
+    if ((e = rkv::launch_rmsnorm(d_x, part, pending, part_stride, g1, a, M, H, eps, stream)) !=
+        hipSuccess)
       return hip_status(e);
     const uint16_t* wqkv[3] = {wq, wk, wv};
+    const uint16_t* aaa[3] = {a, a, a};
     void* cqkv[3] = {q, k, v};
-    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kStoreBf16, wqkv, cqkv, 3, a, M, H, H,
+    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kStoreBf16, wqkv, aaa, cqkv, 3, M, H, H, H,
                               stream)) != hipSuccess)
       return hip_status(e);
     rkv_kv_view lv = *kv;
@@ -474,23 +494,41 @@ int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_st
     if ((rc = attention(&one, rkv::kEncoderFused, d_plan, &lv, q, k, v, att, aws, aws_bytes,
                         hip_stream)))
       return rc;
-    const uint16_t* wos[1] = {wo};
-    void* xs[1] = {d_x};
-    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kAddF32, wos, xs, 1, att, M, H, H, stream)) !=
-        hipSuccess)
+    // output projection in `so` k-slices; x += their sum, a = RMSNorm(x) g2
+    const uint16_t* ws_[rkv::kGemmMaxSet];
+    const uint16_t* xs_[rkv::kGemmMaxSet];
+    void* cs_[rkv::kGemmMaxSet];
+    for (int i = 0; i < so; ++i) {
+      ws_[i] = wo + (size_t)i * (H / so);
+      xs_[i] = att + (size_t)i * (H / so);
+      cs_[i] = part + i * part_stride;
+    }
+    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kStoreF32, ws_, xs_, cs_, so, M, H, H / so, H,
+                              stream)) != hipSuccess)
       return hip_status(e);
-    if ((e = rkv::launch_rmsnorm(d_x, g2, a, M, H, ec->norm_eps, stream)) != hipSuccess)
+    if ((e = rkv::launch_rmsnorm(d_x, part, so, part_stride, g2, a, M, H, eps, stream)) !=
+        hipSuccess)
       return hip_status(e);
     const uint16_t* w1s[1] = {w1};
+    const uint16_t* as[1] = {a};
     void* us[1] = {u};
-    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kGeluBf16, w1s, us, 1, a, M, FF, H, stream)) !=
-        hipSuccess)
+    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kGeluBf16, w1s, as, us, 1, M, FF, H, H,
+                              stream)) != hipSuccess)
       return hip_status(e);
-    const uint16_t* w2s[1] = {w2};
-    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kAddF32, w2s, xs, 1, u, M, H, FF, stream)) !=
-        hipSuccess)
+    for (int i = 0; i < s2; ++i) {
+      ws_[i] = w2 + (size_t)i * (FF / s2);
+      xs_[i] = u + (size_t)i * (FF / s2);
+      cs_[i] = part + i * part_stride;
+    }
+    if ((e = rkv::launch_gemm(rkv::GemmEpilogue::kStoreF32, ws_, xs_, cs_, s2, M, H, FF / s2, FF,
+                              stream)) != hipSuccess)
       return hip_status(e);
+    pending = s2;
   }
+  // the last layer's MLP output into x
+  if ((e = rkv::launch_rmsnorm(d_x, part, pending, part_stride, nullptr, nullptr, M, H, eps,
+                               stream)) != hipSuccess)
+    return hip_status(e);
   return RKV_OK;
 }
 

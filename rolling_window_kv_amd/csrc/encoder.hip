@@ -13,8 +13,11 @@
 // output feature, contiguous in k) is the A operand and the activations (row
 // = token) the B operand, so a lane's result holds four consecutive output
 // features of one token and the epilogue writes them as one vector.  A
-// workgroup of 4 waves computes 64 tokens x 32 features, each wave 16 tokens;
-// the operands of the next two k-steps are in flight while one is computed.
+// workgroup computes 64 tokens x 64 features: both 64 x 64 operand tiles of a
+// k-stage are staged through LDS (double-buffered; the global loads of the
+// next kDepth stages are in flight during a stage's MFMAs), and each of the 4
+// waves computes a 32 x 32 quarter from them, so every loaded element feeds
+// 64 products instead of 16.
 
 #include <math.h>
 
@@ -27,135 +30,247 @@ namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-enum Epilogue { kStoreBf16 = 0, kAddF32 = 1, kGeluBf16 = 2 };
+enum Epilogue { kStoreBf16 = 0, kAddF32 = 1, kGeluBf16 = 2, kStoreF32 = 3 };
 
-// Up to three GEMMs sharing the B operand (the q, k, v projections).
+// Up to four GEMMs launched together: the q, k, v projections (one shared B
+// operand), or the k-slices of one split product.
 struct GemmSet {
-  const uint16_t* w[3];   // [N][K] bfloat16
-  void* c[3];             // [M][N]: bfloat16, or float32 (kAddF32)
+  const uint16_t* w[kGemmMaxSet];   // [N][ld] bfloat16, k from 0 to K
+  const uint16_t* x[kGemmMaxSet];   // [M][ld] bfloat16, k from 0 to K
+  void* c[kGemmMaxSet];             // [M][N]: bfloat16, or float32 (kAddF32, kStoreF32)
 };
 
 __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
 }
 
+constexpr int kTM = 64, kTN = 64, kKS = 64;
+constexpr int kLdk = kKS + 8;      // LDS row stride (elements): 144 B, rows rotate banks
+constexpr int kDepth = 4;          // k-stages whose global loads are in flight
+
 template <int EP>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmSet set, const uint16_t* __restrict__ x,
-                                                   int M, int N, int K) {
-  constexpr int TM = 64, TN = 32, KS = 32;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 15, g4 = lane >> 4;
+__global__ __launch_bounds__(256) void gemm_kernel(GemmSet set, int M, int N, int K, int ld) {
+  __shared__ __attribute__((aligned(16))) uint16_t sw[2][kTN * kLdk];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTM * kLdk];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;          // token half, feature half
   const uint16_t* __restrict__ w = set.w[blockIdx.z];
-  const int n0 = blockIdx.x * TN;
-  const int m0 = blockIdx.y * TM + 16 * wave;
-  const int mrow = m0 + c < M ? m0 + c : M - 1;          // ragged M: clamp, not stored
-  const uint16_t* xr = x + (int64_t)mrow * K + 8 * g4;
-  const uint16_t* w0 = w + (int64_t)(n0 + c) * K + 8 * g4;
-  const uint16_t* w1 = w + (int64_t)(n0 + 16 + c) * K + 8 * g4;
-  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  const int steps = K / KS;
-  u32x4 bx[3], aw0[3], aw1[3];
-  auto load = [&](int i, int slot) {
-    const int k0 = (i < steps ? i : steps - 1) * KS;
-    bx[slot] = ld16(xr + k0);
-    aw0[slot] = ld16(w0 + k0);
-    aw1[slot] = ld16(w1 + k0);
+  const uint16_t* __restrict__ x = set.x[blockIdx.z];
+  const int n0 = blockIdx.x * kTN, m0 = blockIdx.y * kTM;
+  // staging: thread t moves the 16-byte pieces (row t/8 and 32 + t/8, k 8 (t%8))
+  // of both tiles; token rows past M are clamped (read, never stored)
+  const int lr = t >> 3, lk = 8 * (t & 7);
+  const uint16_t* wp0 = w + (int64_t)(n0 + lr) * ld + lk;
+  const uint16_t* wp1 = wp0 + (int64_t)32 * ld;
+  const uint16_t* xp0 = x + (int64_t)min(m0 + lr, M - 1) * ld + lk;
+  const uint16_t* xp1 = x + (int64_t)min(m0 + 32 + lr, M - 1) * ld + lk;
+  const int steps = K / kKS;
+  // register ring: stage s's pieces sit in slot s % kDepth from its load until
+  // its LDS store, which frees the slot for stage s + kDepth
+  u32x4 rw0[kDepth], rw1[kDepth], rx0[kDepth], rx1[kDepth];
+  auto gload = [&](int s, int slot) {
+    const int k0 = (s < steps ? s : steps - 1) * kKS;   // past the end: a harmless reload
+    rw0[slot] = ld16(wp0 + k0);
+    rw1[slot] = ld16(wp1 + k0);
+    rx0[slot] = ld16(xp0 + k0);
+    rx1[slot] = ld16(xp1 + k0);
   };
-  load(0, 0);
-  load(1, 1);
-  for (int i = 0; i < steps; i += 3) {
+  auto lstore = [&](int b, int slot) {
+    *reinterpret_cast<u32x4*>(&sw[b][lr * kLdk + lk]) = rw0[slot];
+    *reinterpret_cast<u32x4*>(&sw[b][(32 + lr) * kLdk + lk]) = rw1[slot];
+    *reinterpret_cast<u32x4*>(&sx[b][lr * kLdk + lk]) = rx0[slot];
+    *reinterpret_cast<u32x4*>(&sx[b][(32 + lr) * kLdk + lk]) = rx1[slot];
+  };
+  f32x4 acc[2][2];
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      if (i + u < steps) {
-        load(i + u + 2, (u + 2) % 3);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aw0[u]),
-                                                       __builtin_bit_cast(bf16x8, bx[u]), acc0,
-                                                       0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aw1[u]),
-                                                       __builtin_bit_cast(bf16x8, bx[u]), acc1,
-                                                       0, 0, 0);
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) gload(d, d);
+  lstore(0, 0);
+  gload(kDepth, 0);
+  __syncthreads();
+  for (int s0 = 0; s0 < steps; s0 += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int s = s0 + u;
+      if (s < steps) {
+        const int b = u & 1;                            // kDepth even: s & 1
+#pragma unroll
+        for (int kk = 0; kk < kKS; kk += 32) {
+          bf16x8 fa[2], fb[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            fa[i] = __builtin_bit_cast(
+                bf16x8,
+                *reinterpret_cast<const u32x4*>(&sw[b][(wn * 32 + 16 * i + c) * kLdk + kk + 8 * g]));
+            fb[i] = __builtin_bit_cast(
+                bf16x8,
+                *reinterpret_cast<const u32x4*>(&sx[b][(wm * 32 + 16 * i + c) * kLdk + kk + 8 * g]));
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+              acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[j][i], 0, 0, 0);
+        }
+        // the LDS buffer written here was last read in stage s - 1, which every
+        // wave finished before the barrier that ended it
+        if (s + 1 < steps) {
+          const int slot = (u + 1) % kDepth;
+          lstore(b ^ 1, slot);
+          if (s + 1 + kDepth < steps) gload(s + 1 + kDepth, slot);
+        }
+        __syncthreads();
       }
     }
   }
-  // lane (c, g4) holds features n0 + 4 g4 + r (acc0) and n0 + 16 + 4 g4 + r
-  // (acc1), r < 4, of token m0 + c
-  const int m = m0 + c;
-  if (m >= M) return;
+  // lane (c, g) of acc[j][i] holds features n0 + 32 wn + 16 i + 4 g + r, r < 4,
+  // of token m0 + 32 wm + 16 j + c
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const f32x4 v = h ? acc1 : acc0;
-    const int n = n0 + 16 * h + 4 * g4;
-    if (EP == kAddF32) {
-      float* p = reinterpret_cast<float*>(set.c[blockIdx.z]) + (int64_t)m * N + n;
-      f32x4 old = *reinterpret_cast<const f32x4*>(p);
-      *reinterpret_cast<f32x4*>(p) = old + v;
-    } else {
-      float e0 = v[0], e1 = v[1], e2 = v[2], e3 = v[3];
-      if (EP == kGeluBf16) {
-        e0 = gelu_erf(e0);
-        e1 = gelu_erf(e1);
-        e2 = gelu_erf(e2);
-        e3 = gelu_erf(e3);
+  for (int j = 0; j < 2; ++j) {
+    const int m = m0 + 32 * wm + 16 * j + c;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const f32x4 v = acc[j][i];
+      const int n = n0 + 32 * wn + 16 * i + 4 * g;
+      if (EP == kAddF32) {
+        float* p = reinterpret_cast<float*>(set.c[blockIdx.z]) + (int64_t)m * N + n;
+        const f32x4 old = *reinterpret_cast<const f32x4*>(p);
+        *reinterpret_cast<f32x4*>(p) = old + v;
+      } else if (EP == kStoreF32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(set.c[blockIdx.z]) + (int64_t)m * N +
+                                  n) = v;
+      } else {
+        float e0 = v[0], e1 = v[1], e2 = v[2], e3 = v[3];
+        if (EP == kGeluBf16) {
+          e0 = gelu_erf(e0);
+          e1 = gelu_erf(e1);
+          e2 = gelu_erf(e2);
+          e3 = gelu_erf(e3);
+        }
+        uint16_t* p = reinterpret_cast<uint16_t*>(set.c[blockIdx.z]) + (int64_t)m * N + n;
+        *reinterpret_cast<u32x2*>(p) = u32x2{cvt2_bf16(e0, e1), cvt2_bf16(e2, e3)};
       }
-      uint16_t* p = reinterpret_cast<uint16_t*>(set.c[blockIdx.z]) + (int64_t)m * N + n;
-      *reinterpret_cast<u32x2*>(p) = u32x2{cvt2_bf16(e0, e1), cvt2_bf16(e2, e3)};
     }
   }
 }
 
-// a[m] = bf16(x[m] / sqrt(mean(x[m]^2) + eps) * g): one wave per token row.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
-                                                      const uint16_t* __restrict__ g,
-                                                      uint16_t* __restrict__ a, int M, int hidden,
-                                                      float eps) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
-  const float* xr = x + (int64_t)m * hidden;
-  float ss = 0.f;
-  for (int i = 2 * lane; i < hidden; i += 128) {
-    const f32x2 v = *reinterpret_cast<const f32x2*>(xr + i);
-    ss = fmaf(v[0], v[0], fmaf(v[1], v[1], ss));
+// x[m] += part_0[m] + ... + part_{NP-1}[m] (in that order), then
+// a[m] = bf16(x[m] / sqrt(mean(x[m]^2) + eps) * g) unless a is null: one
+// workgroup per token row, each thread up to kNormPerThread float4 of it,
+// held in registers throughout; every load of the row is issued at once.
+template <int NP>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
+    float* __restrict__ x, const float* __restrict__ parts, int64_t part_stride,
+    const uint16_t* __restrict__ g, uint16_t* __restrict__ a, int hidden, float eps) {
+  __shared__ float red[kNormThreads / 64];
+  const int t = threadIdx.x;
+  const int n4 = hidden >> 2;
+  const int64_t row = (int64_t)blockIdx.x * hidden;
+  f32x4* xr = reinterpret_cast<f32x4*>(x + row);
+  const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 v[kNormPerThread], pv[NP > 0 ? NP : 1][kNormPerThread];
+#pragma unroll
+  for (int j = 0; j < kNormPerThread; ++j) {
+    const int i = t + kNormThreads * j;
+    v[j] = i < n4 ? xr[i] : zero;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      pv[p][j] = i < n4 ? reinterpret_cast<const f32x4*>(parts + p * part_stride + row)[i] : zero;
   }
+  if (NP > 0) {
+#pragma unroll
+    for (int j = 0; j < kNormPerThread; ++j) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) v[j] += pv[p][j];
+      const int i = t + kNormThreads * j;
+      if (i < n4) xr[i] = v[j];
+    }
+  }
+  if (!a) return;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kNormPerThread; ++j)
+    ss = fmaf(v[j][0], v[j][0], fmaf(v[j][1], v[j][1], fmaf(v[j][2], v[j][2],
+                                                             fmaf(v[j][3], v[j][3], ss))));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  ss = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / 64; ++w) ss += red[w];
   const float r = 1.0f / sqrtf(ss / (float)hidden + eps);
-  uint16_t* ar = a + (int64_t)m * hidden;
-  for (int i = 2 * lane; i < hidden; i += 128) {
-    const f32x2 v = *reinterpret_cast<const f32x2*>(xr + i);
-    const uint32_t gg = *reinterpret_cast<const uint32_t*>(g + i);
-    *reinterpret_cast<uint32_t*>(ar + i) =
-        cvt2_bf16(v[0] * r * bf2f(gg & 0xffffu), v[1] * r * bf2f(gg >> 16));
+  uint16_t* ar = a + row;
+#pragma unroll
+  for (int j = 0; j < kNormPerThread; ++j) {
+    const int i = t + kNormThreads * j;
+    if (i < n4) {
+      const u32x2 gg = *reinterpret_cast<const u32x2*>(g + 4 * i);
+      *reinterpret_cast<u32x2*>(ar + 4 * i) =
+          u32x2{cvt2_bf16(v[j][0] * r * bf2f(gg[0] & 0xffffu), v[j][1] * r * bf2f(gg[0] >> 16)),
+                cvt2_bf16(v[j][2] * r * bf2f(gg[1] & 0xffffu), v[j][3] * r * bf2f(gg[1] >> 16))};
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_rmsnorm(const float* x, const uint16_t* g, uint16_t* a, int M, int hidden,
-                          float eps, hipStream_t stream) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3((M + 3) / 4), dim3(256), 0, stream, x, g, a, M, hidden,
-                     eps);
+hipError_t launch_rmsnorm(float* x, const float* parts, int nparts, int64_t part_stride,
+                          const uint16_t* g, uint16_t* a, int M, int hidden, float eps,
+                          hipStream_t stream) {
+  const dim3 grid(M), block(kNormThreads);
+  switch (nparts) {
+    case 0:
+      hipLaunchKernelGGL(rmsnorm_kernel<0>, grid, block, 0, stream, x, parts, part_stride, g, a,
+                         hidden, eps);
+      break;
+    case 1:
+      hipLaunchKernelGGL(rmsnorm_kernel<1>, grid, block, 0, stream, x, parts, part_stride, g, a,
+                         hidden, eps);
+      break;
+    case 2:
+      hipLaunchKernelGGL(rmsnorm_kernel<2>, grid, block, 0, stream, x, parts, part_stride, g, a,
+                         hidden, eps);
+      break;
+    case 4:
+      hipLaunchKernelGGL(rmsnorm_kernel<4>, grid, block, 0, stream, x, parts, part_stride, g, a,
+                         hidden, eps);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(GemmEpilogue ep, const uint16_t* const* w, void* const* c, int count,
-                       const uint16_t* x, int M, int N, int K, hipStream_t stream) {
+hipError_t launch_gemm(GemmEpilogue ep, const uint16_t* const* w, const uint16_t* const* x,
+                       void* const* c, int count, int M, int N, int K, int ld,
+                       hipStream_t stream) {
   GemmSet set{};
   for (int i = 0; i < count; ++i) {
     set.w[i] = w[i];
+    set.x[i] = x[i];
     set.c[i] = c[i];
   }
-  const dim3 grid(N / 32, (M + 63) / 64, count);
+  const dim3 grid(N / kTN, (M + kTM - 1) / kTM, count);
   switch (ep) {
     case GemmEpilogue::kStoreBf16:
-      hipLaunchKernelGGL((gemm_kernel<kStoreBf16>), grid, dim3(256), 0, stream, set, x, M, N, K);
+      hipLaunchKernelGGL((gemm_kernel<kStoreBf16>), grid, dim3(256), 0, stream, set, M, N, K, ld);
       break;
     case GemmEpilogue::kAddF32:
-      hipLaunchKernelGGL((gemm_kernel<kAddF32>), grid, dim3(256), 0, stream, set, x, M, N, K);
+      hipLaunchKernelGGL((gemm_kernel<kAddF32>), grid, dim3(256), 0, stream, set, M, N, K, ld);
+      break;
+    case GemmEpilogue::kGeluBf16:
+      hipLaunchKernelGGL((gemm_kernel<kGeluBf16>), grid, dim3(256), 0, stream, set, M, N, K, ld);
       break;
     default:
-      hipLaunchKernelGGL((gemm_kernel<kGeluBf16>), grid, dim3(256), 0, stream, set, x, M, N, K);
+      hipLaunchKernelGGL((gemm_kernel<kStoreF32>), grid, dim3(256), 0, stream, set, M, N, K, ld);
       break;
   }
   return hipGetLastError();

@@ -266,13 +266,18 @@ def test_encoder_step_sizes_and_validation(rkv):
                                                                 + 2 * hidden * ffn)
     ws = rkv.rkv_encoder_step_workspace_bytes(cfg, ec, slots)
     assert ws >= 2 * S * F * (5 * hidden + ffn)
-    bad = [rkv.make_encoder_cfg(ffn=48), rkv.make_encoder_cfg(ffn=0),
+    bad = [rkv.make_encoder_cfg(ffn=48), rkv.make_encoder_cfg(ffn=96), rkv.make_encoder_cfg(ffn=0),
            rkv.make_encoder_cfg(norm_eps=-1.0), rkv.make_encoder_cfg(norm_eps=float("nan"))]
     for b in bad:
         assert rkv.rkv_encoder_layer_weight_bytes(cfg, b) == 0
         assert rkv.rkv_encoder_step_workspace_bytes(cfg, b, slots) == 0
     dec = good_cfg(rkv)
     assert rkv.rkv_encoder_layer_weight_bytes(dec, ec) == 0
+    for heads, dim in ((1, 32), (65, 64)):      # hidden 32: not a multiple of 64; 4160 > 4096
+        wide = rkv.make_cfg(S, L, num_q_heads=heads, num_kv_heads=heads, head_dim=dim,
+                            mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F)
+        if rkv.rkv_validate_cfg(wide) == rkv.RKV_OK:
+            assert rkv.rkv_encoder_layer_weight_bytes(wide, ec) == 0
     assert rkv.rkv_encoder_step_workspace_bytes(cfg, ec, 0) == 0
     kv = rkv.rkv_kv_view(FAKE, FAKE + 0x1000000, None, S * H * slots * d, H * slots * d,
                          slots * d, d, slots, 0)
