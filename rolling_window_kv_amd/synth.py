@@ -106,3 +106,14 @@ def encoder_stack_inputs(seed, streams, period, frames, hidden):
     rng = np.random.default_rng([int(seed), 2 ** 31 - 2])
     return torch.from_numpy(rng.standard_normal((period, streams, frames, hidden),
                                                 dtype=np.float32))
+
+
+def tcond_weights(seed, layers, hidden, dim, max_frame_len=8):
+    """Synthetic delay-conditioning weights (CPU bf16): the frame-length table
+    [max_frame_len + 1, dim] = N(0, 1) and per layer the modulation matrix
+    [layers, 2 hidden, dim] = 0.1 N(0, 1) / sqrt(dim) (rows: scale, then shift)."""
+    rng = np.random.default_rng([int(seed), 2 ** 31 - 3])
+    table = rng.standard_normal((max_frame_len + 1, dim), dtype=np.float32)
+    A = rng.standard_normal((layers, 2 * hidden, dim), dtype=np.float32) * np.float32(
+        0.1 / np.sqrt(dim))
+    return (torch.from_numpy(table).to(torch.bfloat16), torch.from_numpy(A).to(torch.bfloat16))
