@@ -207,7 +207,7 @@ def build_inputs(c, seed, dev):
 
 def run_gpu(c, args):
     import torch
-    from rolling_window_kv_amd import rkv
+    from rolling_window_kv_amd import rkv, synth
     rkv.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -250,6 +250,21 @@ def run_gpu(c, args):
 
     pipelined = args.path == "pipelined" and c["mode"] != "enc"
     plans = [cache.plan, cache.plan_next]
+    tcond = None
+    if args.tcond:
+        # delay conditioning after each step's attention: the 8 post-trained
+        # (clock, delay) settings, streams spread over them
+        settings = [(240, 80), (320, 80), (480, 80), (560, 80), (240, 120), (480, 120),
+                    (320, 160), (480, 160)]
+        conds = [rkv.rkv_tcond_delay_tokens(dl, ck) for dl, ck in settings]
+        table, A = synth.tcond_weights(7, L, cfg.num_q_heads * cfg.head_dim, 256)
+        tc = rkv.make_tcond_cfg(L, cfg.num_q_heads * cfg.head_dim, dim=256,
+                                num_conds=len(conds), max_frame_len=8)
+        mod = torch.empty((L, len(conds), 2, tc.hidden), dtype=torch.float32, device=dev)
+        rkv.rkv_tcond_prepare(tc, [n for n, _ in conds], [f for _, f in conds], table.to(dev),
+                              A.to(dev), mod, sp)
+        cond = torch.arange(S, dtype=torch.int32, device=dev) % len(conds)
+        tcond = (tc, mod, cond)
 
     def step(i, ev=None):
         j = i % P
@@ -265,6 +280,8 @@ def run_gpu(c, args):
                                           v[j], out, ws, sp)
             if ev is not None:
                 ev[1].record(stream)
+            if tcond is not None:
+                rkv.rkv_tcond_modulate(cfg, tcond[0], tcond[1], tcond[2], out, sp)
             return
         rkv.rkv_advance(cfg, cache.state, cache.plan, sp)
         if c["mode"] == "compact":
@@ -282,6 +299,8 @@ def run_gpu(c, args):
             rkv.rkv_decode_step(cfg, cache.plan, cache.kv, q[j], k[j], v[j], out, ws, sp)
         if ev is not None:
             ev[1].record(stream)
+        if tcond is not None:
+            rkv.rkv_tcond_modulate(cfg, tcond[0], tcond[1], tcond[2], out, sp)
 
     def fill(i):
         # Untimed set-up: the same cache updates as a step, without attention
@@ -319,7 +338,7 @@ def run_gpu(c, args):
     # the attention launch of every RUN-th step.
     K = args.steps
     RUN, GAP = 8, 4
-    bracket = pipelined and c["mode"] == "rebase" and K >= RUN
+    bracket = pipelined and c["mode"] == "rebase" and K >= RUN and tcond is None
     ev_runs, ev_steps = {}, {}
     if args.kernel_events:
         for n in (range(0, K - RUN + 1, RUN * GAP) if bracket else range(0, K, RUN)):
@@ -541,6 +560,9 @@ def main():
     ap.add_argument("--encoder-stack", type=int, default=0, metavar="STREAMS",
                     help="time the 32-layer incremental encoder step for STREAMS streams "
                          "instead")
+    ap.add_argument("--tcond", action="store_true",
+                    help="apply the delay conditioning (rkv_tcond_modulate) to every step's "
+                         "attention output (decoder workloads)")
     ap.add_argument("--kv-fp16", action="store_true",
                     help="store K and V as fp16 (the fp16 cache variant; decoder workloads)")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
@@ -579,6 +601,9 @@ def main():
         print(json.dumps(run_encoder_stack(args)), flush=True)
         return
     c = dict(CONFIGS[args.config])
+    if args.tcond and c["mode"] == "enc":
+        print("--tcond: delay conditioning applies to the decoder workloads", file=sys.stderr)
+        sys.exit(2)
     if args.kv_fp16 and c["mode"] == "enc":
         print("--kv-fp16: the encoder cache is bfloat16 only", file=sys.stderr)
         sys.exit(2)
@@ -625,14 +650,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": c["name"], "layers": L, "streams": S,
                    "path": args.path if c["mode"] != "enc" else "fused",
-                   "alg_bytes_per_stream_layer_step": b_sl},
+                   "alg_bytes_per_stream_layer_step": b_sl,
+                   **({"tcond": "rkv_tcond_modulate after each step, 8 settings, dim 256"}
+                      if args.tcond else {})},
         "achieved_GBps_step": round(step_gbps, 1),
         "hbm_frac_step": round(step_gbps / PEAK_HBM_GBPS, 4),
         "clock_steps_per_s": round(K / secs, 1),
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if args.cpu and not args.kv_fp16:
+    if args.cpu and not args.kv_fp16 and not args.tcond:
         res["cpu_baseline"] = cpu_baseline(c, 1000 + args.config, args.cpu_budget)
     print(json.dumps(res), flush=True)
 

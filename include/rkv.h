@@ -442,6 +442,64 @@ int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_st
                      const rkv_kv_view* kv, const void* d_weights, float* d_x,
                      void* d_workspace, size_t workspace_bytes, void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Delay conditioning (Audio8 ASR Infinite explainer, 可配置转写延迟; model
+ * card, 优化操作点 and 架构).  The decoder is told how many clock steps it runs
+ * behind real time, num_delay_tokens = target_delay_ms / clock; that count
+ * as a sinusoidal embedding plus a learned frame-length embedding row is the
+ * condition vector t_cond, which modulates the hidden state after the
+ * attention of every decoder layer.  The sources do not give the form of the
+ * modulation; it is taken here as a feature-wise scale and shift of the
+ * layer's attention output (num_q_heads * head_dim features):
+ *   h <- h (1 + gamma_l) + beta_l,   [gamma_l; beta_l] = A_l t_cond,
+ *   t_cond = e(n) + table[frame_len],
+ *   e_i = sin(n w_i), e_{D/2+i} = cos(n w_i), w_i = 10000^(-2i/D), i < D/2.
+ * ------------------------------------------------------------------------- */
+
+#define RKV_TCOND_MAX_CONDS 64
+#define RKV_TCOND_MAX_DIM 1024
+
+typedef struct rkv_tcond_cfg {
+  int32_t num_layers;     /* L */
+  int32_t hidden;         /* modulated features per row: a multiple of 8 */
+  int32_t dim;            /* D: width of t_cond, even, 2 .. RKV_TCOND_MAX_DIM */
+  int32_t num_conds;      /* C: distinct (delay, frame_len) settings, 1 .. RKV_TCOND_MAX_CONDS */
+  int32_t max_frame_len;  /* the frame-length table has max_frame_len + 1 rows, >= 0 */
+  int32_t reserved[3];
+} rkv_tcond_cfg;
+
+/* Host only: num_delay_tokens and frame_len (20 ms tower frames per step)
+ * for a delay and an audio clock.  RKV_EINVAL for a clock other than 80, 120
+ * or 160 ms, a delay that is not a positive integer multiple of the clock,
+ * or a null output. */
+int rkv_tcond_delay_tokens(int32_t target_delay_ms, int32_t clock_ms, int32_t* num_delay_tokens,
+                           int32_t* frame_len);
+
+/* Modulation vectors of every (layer, condition), once per change of the
+ * settings (not per step): d_mod [L][C][2][hidden] float32 (device; gamma,
+ * then beta) from h_num_delay[C] >= 0 and h_frame_len[C] in
+ * [0, max_frame_len] (host arrays, passed in the launch), the frame-length
+ * table d_frame_table [max_frame_len + 1][dim] and the matrices d_weights
+ * [L][2 hidden][dim] (device, bfloat16; the gamma rows of A_l first).
+ * t_cond in float32 from float64 sin/cos; products summed in float32.
+ * Errors: RKV_EINVAL (bad cfg, null pointer, count or frame_len out of
+ * range), RKV_EALIGN (a device pointer not 16-byte aligned), RKV_EHIP. */
+int rkv_tcond_prepare(const rkv_tcond_cfg* tc, const int32_t* h_num_delay,
+                      const int32_t* h_frame_len, const void* d_frame_table,
+                      const void* d_weights, float* d_mod, void* hip_stream);
+
+/* Per clock step, after the decoder attention: out <- out (1 + gamma) + beta,
+ * in place, for every (layer, stream) row of d_out [L][S][num_q_heads]
+ * [head_dim] (bfloat16, rounded to nearest even, or float32 with
+ * RKV_F_OUT_F32), with the modulation of condition d_stream_cond[s] (device
+ * int32 [S]).  A stream whose index lies outside [0, num_conds) is left as it
+ * is (a negative index switches conditioning off for that stream).  tc must
+ * match cfg: tc->num_layers == num_layers, tc->hidden == num_q_heads *
+ * head_dim.  Errors: RKV_EINVAL (bad cfg or tc, mismatch, null pointer),
+ * RKV_EALIGN (d_mod or d_out not 16-byte aligned), RKV_EHIP. */
+int rkv_tcond_modulate(const rkv_cfg* cfg, const rkv_tcond_cfg* tc, const float* d_mod,
+                       const int32_t* d_stream_cond, void* d_out, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

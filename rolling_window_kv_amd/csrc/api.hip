@@ -7,6 +7,7 @@
 #include "rkv_internal.h"
 #include "rkv_encoder.h"
 #include "rkv_mel.h"
+#include "rkv_tcond.h"
 
 namespace {
 
@@ -547,3 +548,61 @@ static_assert(sizeof(rkv_stream_state) == 48, "rkv_stream_state layout");
 static_assert(offsetof(rkv_step_plan, rope_new) == 128, "rkv_step_plan header");
 static_assert(sizeof(rkv_step_plan) == 128 + 8192 + 1024, "rkv_step_plan layout");
 static_assert(sizeof(rkv_kv_view) == 64, "rkv_kv_view layout");
+
+// ---------------------------------------------------------------------------
+// Delay conditioning
+// ---------------------------------------------------------------------------
+
+static int check_tcond(const rkv_tcond_cfg* tc) {
+  if (!tc) return RKV_EINVAL;
+  if (tc->num_layers < 1 || tc->hidden < 8 || tc->hidden % 8) return RKV_EINVAL;
+  if (tc->dim < 2 || tc->dim % 2 || tc->dim > RKV_TCOND_MAX_DIM) return RKV_EINVAL;
+  if (tc->num_conds < 1 || tc->num_conds > RKV_TCOND_MAX_CONDS) return RKV_EINVAL;
+  if (tc->max_frame_len < 0 || tc->max_frame_len > (1 << 16)) return RKV_EINVAL;
+  return RKV_OK;
+}
+
+int rkv_tcond_delay_tokens(int32_t target_delay_ms, int32_t clock_ms, int32_t* num_delay_tokens,
+                           int32_t* frame_len) {
+  if (!num_delay_tokens || !frame_len) return RKV_EINVAL;
+  if (clock_ms != 80 && clock_ms != 120 && clock_ms != 160) return RKV_EINVAL;
+  if (target_delay_ms <= 0 || target_delay_ms % clock_ms) return RKV_EINVAL;
+  *num_delay_tokens = target_delay_ms / clock_ms;
+  *frame_len = clock_ms / 20;
+  return RKV_OK;
+}
+
+int rkv_tcond_prepare(const rkv_tcond_cfg* tc, const int32_t* h_num_delay,
+                      const int32_t* h_frame_len, const void* d_frame_table,
+                      const void* d_weights, float* d_mod, void* hip_stream) {
+  int rc = check_tcond(tc);
+  if (rc) return rc;
+  if (!h_num_delay || !h_frame_len) return RKV_EINVAL;
+  if ((rc = check_ptr(d_frame_table)) || (rc = check_ptr(d_weights)) || (rc = check_ptr(d_mod)))
+    return rc;
+  rkv::TcondConds conds{};
+  for (int c = 0; c < tc->num_conds; ++c) {
+    if (h_num_delay[c] < 0 || h_num_delay[c] > (1 << 24)) return RKV_EINVAL;
+    if (h_frame_len[c] < 0 || h_frame_len[c] > tc->max_frame_len) return RKV_EINVAL;
+    conds.num_delay[c] = h_num_delay[c];
+    conds.frame_len[c] = h_frame_len[c];
+  }
+  return hip_status(rkv::launch_tcond_prepare(tc, conds, static_cast<const uint16_t*>(d_frame_table),
+                                              static_cast<const uint16_t*>(d_weights), d_mod,
+                                              static_cast<hipStream_t>(hip_stream)));
+}
+
+int rkv_tcond_modulate(const rkv_cfg* cfg, const rkv_tcond_cfg* tc, const float* d_mod,
+                       const int32_t* d_stream_cond, void* d_out, void* hip_stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if ((rc = check_tcond(tc))) return rc;
+  const int hidden = cfg->num_q_heads * cfg->head_dim;
+  if (tc->num_layers != cfg->num_layers || tc->hidden != hidden) return RKV_EINVAL;
+  if (!d_stream_cond) return RKV_EINVAL;
+  if ((rc = check_ptr(d_mod)) || (rc = check_ptr(d_out))) return rc;
+  return hip_status(rkv::launch_tcond_modulate(
+      cfg->num_layers, cfg->num_streams, hidden, tc->num_conds,
+      (cfg->flags & RKV_F_OUT_F32) != 0, d_mod, d_stream_cond, d_out,
+      static_cast<hipStream_t>(hip_stream)));
+}

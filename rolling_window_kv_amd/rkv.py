@@ -43,7 +43,11 @@ ENTRY_POINTS = (
     "rkv_encoder_chunk_attn", "rkv_reset_streams", "rkv_restart_step",
     "rkv_mel_filters_host", "rkv_mel_step",
     "rkv_encoder_layer_weight_bytes", "rkv_encoder_step_workspace_bytes", "rkv_encoder_step",
+    "rkv_tcond_delay_tokens", "rkv_tcond_prepare", "rkv_tcond_modulate",
 )
+
+RKV_TCOND_MAX_CONDS = 64
+RKV_TCOND_MAX_DIM = 1024
 
 RKV_STREAM_MAX_DECODE_KV = 2000
 RKV_RESTART_NONE = 0
@@ -86,6 +90,12 @@ class rkv_kv_view(ctypes.Structure):
 class rkv_encoder_cfg(ctypes.Structure):
     _fields_ = [("ffn", ctypes.c_int32), ("norm_eps", ctypes.c_float),
                 ("reserved", ctypes.c_int32 * 2)]
+
+
+class rkv_tcond_cfg(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("num_conds", ctypes.c_int32),
+                ("max_frame_len", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class rkv_mel_cfg(ctypes.Structure):
@@ -164,6 +174,11 @@ def lib():
             "rkv_encoder_step_workspace_bytes": ([pc, ctypes.POINTER(rkv_encoder_cfg), i32], sz),
             "rkv_encoder_step": ([pc, ctypes.POINTER(rkv_encoder_cfg), vp, pk, vp, vp, vp, sz, vp],
                                  ctypes.c_int),
+            "rkv_tcond_delay_tokens": ([i32, i32, vp, vp], ctypes.c_int),
+            "rkv_tcond_prepare": ([ctypes.POINTER(rkv_tcond_cfg), vp, vp, vp, vp, vp, vp],
+                                  ctypes.c_int),
+            "rkv_tcond_modulate": ([pc, ctypes.POINTER(rkv_tcond_cfg), vp, vp, vp, vp],
+                                   ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -334,6 +349,38 @@ def rkv_encoder_step(cfg, ecfg, plan, kv, weights, x, workspace, stream=None):
            lib().rkv_encoder_step(ctypes.byref(cfg), ctypes.byref(ecfg), _ptr(plan),
                                   ctypes.byref(kv), _ptr(weights), _ptr(x), _ptr(workspace),
                                   nbytes, _stream(stream)))
+
+
+def make_tcond_cfg(num_layers, hidden, dim=256, num_conds=1, max_frame_len=8) -> rkv_tcond_cfg:
+    return rkv_tcond_cfg(num_layers, hidden, dim, num_conds, max_frame_len,
+                         (ctypes.c_int32 * 3)(0, 0, 0))
+
+
+def rkv_tcond_delay_tokens(target_delay_ms, clock_ms):
+    """(num_delay_tokens, frame_len) for a delay and an audio clock (host)."""
+    n, f = ctypes.c_int32(), ctypes.c_int32()
+    _check("rkv_tcond_delay_tokens",
+           lib().rkv_tcond_delay_tokens(int(target_delay_ms), int(clock_ms), ctypes.byref(n),
+                                        ctypes.byref(f)))
+    return n.value, f.value
+
+
+def rkv_tcond_prepare(tc, num_delay, frame_len, table, weights, mod, stream=None):
+    """num_delay, frame_len: host sequences of tc.num_conds ints; table, weights:
+    bfloat16 device tensors; mod: float32 [L, C, 2, hidden] device tensor."""
+    n = np.ascontiguousarray(num_delay, dtype=np.int32)
+    f = np.ascontiguousarray(frame_len, dtype=np.int32)
+    if n.size != tc.num_conds or f.size != tc.num_conds:
+        raise ValueError("one delay count and frame_len per condition")
+    _check("rkv_tcond_prepare",
+           lib().rkv_tcond_prepare(ctypes.byref(tc), n.ctypes.data, f.ctypes.data, _ptr(table),
+                                   _ptr(weights), _ptr(mod), _stream(stream)))
+
+
+def rkv_tcond_modulate(cfg, tc, mod, stream_cond, out, stream=None):
+    _check("rkv_tcond_modulate",
+           lib().rkv_tcond_modulate(ctypes.byref(cfg), ctypes.byref(tc), _ptr(mod),
+                                    _ptr(stream_cond), _ptr(out), _stream(stream)))
 
 
 def make_mel_cfg(num_streams, n_fft=400, hop=160, n_mels=128,

@@ -297,3 +297,43 @@ def test_encoder_step_sizes_and_validation(rkv):
     assert step(ctypes.byref(dec), e, P, k, W, X, WS, ws, N) == rkv.RKV_EINVAL
     assert step(c, ctypes.byref(bad[0]), P, k, W, X, WS, ws, N) == rkv.RKV_EINVAL
     assert rkv.rkv_last_hip_error() == 0
+
+
+def test_tcond_sizes_and_validation(rkv):
+    assert ctypes.sizeof(rkv.rkv_tcond_cfg) == 32
+    L, C = 2, 3
+    cfg = good_cfg(rkv, num_layers=L)                       # 16 x 128 = 2048 features
+    tc = rkv.make_tcond_cfg(L, 2048, dim=256, num_conds=C, max_frame_len=8)
+    n = np.array([6, 3, 2], np.int32)
+    f = np.array([4, 6, 8], np.int32)
+    F = ctypes.c_void_p(FAKE)
+    M = ctypes.c_void_p(MISALIGNED)
+    N = None
+    prep = lambda t, nn, ff, a, b, c: call(rkv, "rkv_tcond_prepare", t, nn, ff, a, b, c, N)
+    t = ctypes.byref(tc)
+    assert prep(N, n.ctypes.data, f.ctypes.data, F, F, F) == rkv.RKV_EINVAL
+    assert prep(t, N, f.ctypes.data, F, F, F) == rkv.RKV_EINVAL
+    assert prep(t, n.ctypes.data, f.ctypes.data, F, F, N) == rkv.RKV_EINVAL
+    assert prep(t, n.ctypes.data, f.ctypes.data, M, F, F) == rkv.RKV_EALIGN
+    assert prep(t, n.ctypes.data, f.ctypes.data, F, F, M) == rkv.RKV_EALIGN
+    bad_f = np.array([4, 9, 8], np.int32)                    # beyond the 9-row table
+    assert prep(t, n.ctypes.data, bad_f.ctypes.data, F, F, F) == rkv.RKV_EINVAL
+    bad_n = np.array([6, -1, 2], np.int32)
+    assert prep(t, bad_n.ctypes.data, f.ctypes.data, F, F, F) == rkv.RKV_EINVAL
+    for kw in (dict(dim=255), dict(dim=0), dict(dim=2048), dict(num_conds=0),
+               dict(num_conds=65), dict(hidden=12), dict(max_frame_len=-1)):
+        args = dict(num_layers=L, hidden=2048, dim=256, num_conds=C, max_frame_len=8)
+        args.update(kw)
+        bad = rkv.make_tcond_cfg(**args)
+        assert prep(ctypes.byref(bad), n.ctypes.data, f.ctypes.data, F, F, F) == rkv.RKV_EINVAL
+    mod = lambda c, t_, a, b, o: call(rkv, "rkv_tcond_modulate", c, t_, a, b, o, N)
+    c = ctypes.byref(cfg)
+    assert mod(c, t, F, N, F) == rkv.RKV_EINVAL
+    assert mod(c, t, F, F, M) == rkv.RKV_EALIGN
+    assert mod(c, t, M, F, F) == rkv.RKV_EALIGN
+    other = rkv.make_tcond_cfg(L + 1, 2048, dim=256, num_conds=C)
+    assert mod(c, ctypes.byref(other), F, F, F) == rkv.RKV_EINVAL
+    narrow = rkv.make_tcond_cfg(L, 1024, dim=256, num_conds=C)
+    assert mod(c, ctypes.byref(narrow), F, F, F) == rkv.RKV_EINVAL
+    assert mod(N, t, F, F, F) == rkv.RKV_EINVAL
+    assert rkv.rkv_last_hip_error() == 0
