@@ -47,7 +47,10 @@ CONFIGS = {
     3: dict(name="36 layers x 256 streams, W mix 375/250/188 (86/85/85), re-base chunk 25, "
                  "start offsets U[0,5000], 1% x8 outliers",
             mode="rebase", L=36, S=256, W=(375, 250, 188), dc=25, comp=False, period=16,
-            steps=600, warmup=50, outlier=0.01, offsets=5000),
+            steps=600, warmup=50, outlier=0.01, offsets=5000,
+            # staggered starts: a few streams re-base in every step, which the
+            # dense update launch handles better than the in-attention write-back
+            path="update"),
     4: dict(name="26 layers x 16 streams, 16q/2kv d128 bf16, window 8192, capacity 9216, "
                  "logical-offset compaction",
             mode="compact", L=26, S=16, W=8192, cap=9216, period=16, steps=1024, warmup=16),
@@ -229,24 +232,24 @@ def run_gpu(c, args):
             windows = np.full(S, c["W"], np.int32)
             origins = np.zeros(S, np.int64)
         slots = int(windows.max())
-        cache = rkv.Cache(cfg, slots, windows, windows, origins, device=dev, zero=False)
+        cache = rkv.Cache(cfg, slots, windows, windows, origins, device=dev, zero=False, layout=args.layout)
         prefill = slots
     elif c["mode"] == "compact":
         cfg = rkv.make_cfg(S, L, mode=rkv.RKV_MODE_COMPACT, flags=kv_flags)
-        cache = rkv.Cache(cfg, c["cap"], c["W"], c["cap"], 0, device=dev, zero=False)
+        cache = rkv.Cache(cfg, c["cap"], c["W"], c["cap"], 0, device=dev, zero=False, layout=args.layout)
         prefill = c["cap"]
     else:
         cfg = rkv.make_cfg(S, L, num_q_heads=c["H"], num_kv_heads=c["H"], head_dim=c["d"],
                            mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=c["F"])
         cap = c["W"] + c["F"]
-        cache = rkv.Cache(cfg, cap, c["W"], cap, 0, device=dev, zero=False)
+        cache = rkv.Cache(cfg, cap, c["W"], cap, 0, device=dev, zero=False, layout=args.layout)
         prefill = (cap + c["F"] - 1) // c["F"]
     out = torch.empty(q.shape[1:], dtype=torch.bfloat16, device=dev)
     P = q.shape[0]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     ws = cache.workspace
-    separate = args.path == "separate"
+    separate = args.path in ("separate", "update")
 
     pipelined = args.path == "pipelined" and c["mode"] != "enc"
     plans = [cache.plan, cache.plan_next]
@@ -290,6 +293,9 @@ def run_gpu(c, args):
             ev[0].record(stream)
         if c["mode"] == "enc":
             rkv.rkv_encoder_chunk_attn(cfg, cache.plan, cache.kv, q[j], k[j], v[j], out, ws, sp)
+        elif args.path == "update":
+            rkv.rkv_update_step(cfg, cache.plan, cache.kv, k[j], v[j], sp)
+            rkv.rkv_decode_attn(cfg, cache.plan, cache.kv, q[j], out, ws, sp)
         elif separate:
             if c["mode"] == "rebase":
                 rkv.rkv_roll_rebase(cfg, cache.plan, cache.kv, sp)
@@ -548,18 +554,25 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS))
-    ap.add_argument("--path", choices=("pipelined", "fused", "separate"), default="pipelined",
-                    help="pipelined: rkv_decode_step_pipelined (the step plan of the next "
+    ap.add_argument("--path", choices=("pipelined", "fused", "separate", "update"),
+                    default=None,
+                    help="default: update for workload 3, pipelined otherwise.  "
+                         "pipelined: rkv_decode_step_pipelined (the step plan of the next "
                          "step computed in the same launch); fused: rkv_advance + "
                          "rkv_decode_step; separate: rkv_advance + rkv_roll_rebase + "
-                         "rkv_append + rkv_decode_attn (encoder workloads: always "
-                         "rkv_advance + rkv_encoder_chunk_attn)")
+                         "rkv_append + rkv_decode_attn; update: rkv_advance + "
+                         "rkv_update_step (re-base and append in one launch) + "
+                         "rkv_decode_attn (encoder workloads: always rkv_advance + "
+                         "rkv_encoder_chunk_attn)")
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
     ap.add_argument("--mel", type=int, default=0, metavar="STREAMS",
                     help="time the rolling log-mel front end for STREAMS streams instead")
     ap.add_argument("--encoder-stack", type=int, default=0, metavar="STREAMS",
                     help="time the 32-layer incremental encoder step for STREAMS streams "
                          "instead")
+    ap.add_argument("--layout", choices=("interleaved", "separate"), default="interleaved",
+                    help="ring layout: K and V rows of a slot side by side (interleaved) or "
+                         "K and V in separate buffers")
     ap.add_argument("--tcond", action="store_true",
                     help="apply the delay conditioning (rkv_tcond_modulate) to every step's "
                          "attention output (decoder workloads)")
@@ -607,6 +620,7 @@ def main():
     if args.kv_fp16 and c["mode"] == "enc":
         print("--kv-fp16: the encoder cache is bfloat16 only", file=sys.stderr)
         sys.exit(2)
+    args.path = c.get("path", "pipelined") if args.path is None else args.path
     args.steps = c["steps"] if args.steps is None else args.steps
     args.warmup = c["warmup"] if args.warmup is None else args.warmup
 
@@ -621,13 +635,17 @@ def main():
               "enc": "attn_kernel<64,4,encoder_fused>"}[c["mode"]]
     if args.path == "separate" and c["mode"] != "enc":
         kernel = "rebase+append+attn_kernel<128,4,decode_read>"
+    if args.path == "update" and c["mode"] != "enc":
+        kernel = "update+attn_kernel<128,4,decode_read>"
     if args.kv_fp16:
         kernel = kernel.replace(">", ",fp16>")
     roofline = None
     if r["kernel_ms"]:
         per_launch = b_sl * L * S
         achieved = per_launch / (r["kernel_ms"] / 1e3) / 1e9
-        traffic = load_traffic(kernel, f"config{args.config}")
+        # the stored counter figures were taken with the interleaved layout
+        traffic = (load_traffic(kernel, f"config{args.config}")
+                   if args.layout == "interleaved" else None)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                     "traffic": traffic, "kernel": kernel,
@@ -651,6 +669,7 @@ def main():
         "config": {"workload": c["name"], "layers": L, "streams": S,
                    "path": args.path if c["mode"] != "enc" else "fused",
                    "alg_bytes_per_stream_layer_step": b_sl,
+                   **({"layout": args.layout} if args.layout != "interleaved" else {}),
                    **({"tcond": "rkv_tcond_modulate after each step, 8 settings, dim 256"}
                       if args.tcond else {})},
         "achieved_GBps_step": round(step_gbps, 1),

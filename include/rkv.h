@@ -223,6 +223,16 @@ int rkv_append(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
 int rkv_roll_rebase(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
                     const rkv_kv_view* kv, void* hip_stream);
 
+/* The cache updates of one step in one launch: the re-base of rkv_roll_rebase
+ * (for the streams whose base moves) and the append of rkv_append, with the
+ * same ring contents as those two calls in that order (the re-base skips the
+ * new row's slot, the append writes only it, so the two are independent).
+ * Any mode (COMPACT and ENC_CHUNK plans never move the base; in COMPACT mode
+ * call rkv_compact first).  Arguments and errors as rkv_append. */
+int rkv_update_step(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
+                    const rkv_kv_view* kv, const void* k_new, const void* v_new,
+                    void* hip_stream);
+
 /* Compaction (voxtral.c explainer section 二): for streams whose plan has
  * compact_drop D > 0, move K and V rows [D, D + window) to [0, window) in
  * row order (an overlapping forward move, done in place).  COMPACT mode only;

@@ -8,6 +8,7 @@
 #include "rkv_encoder.h"
 #include "rkv_mel.h"
 #include "rkv_tcond.h"
+#include "rkv_update.h"
 
 namespace {
 
@@ -354,6 +355,18 @@ int rkv_roll_rebase(const rkv_cfg* cfg, const rkv_step_plan* d_plan, const rkv_k
   if ((rc = check_kv(cfg, kv))) return rc;
   if (!d_plan) return RKV_EINVAL;
   return hip_status(rkv::launch_rebase(cfg, d_plan, ring_of(kv), static_cast<hipStream_t>(hip_stream)));
+}
+
+int rkv_update_step(const rkv_cfg* cfg, const rkv_step_plan* d_plan, const rkv_kv_view* kv,
+                    const void* k_new, const void* v_new, void* hip_stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if ((rc = check_kv(cfg, kv))) return rc;
+  if (!d_plan) return RKV_EINVAL;
+  if ((rc = check_ptr(k_new)) || (rc = check_ptr(v_new))) return rc;
+  return hip_status(rkv::launch_update(cfg, d_plan, ring_of(kv), static_cast<const uint16_t*>(k_new),
+                                       static_cast<const uint16_t*>(v_new),
+                                       static_cast<hipStream_t>(hip_stream)));
 }
 
 int rkv_compact(const rkv_cfg* cfg, const rkv_step_plan* d_plan, const rkv_kv_view* kv,

@@ -38,7 +38,7 @@ RKV_MAX_HEAD_DIM = 128
 ENTRY_POINTS = (
     "rkv_version", "rkv_strerror", "rkv_last_hip_error", "rkv_validate_cfg",
     "rkv_state_init_host", "rkv_state_init", "rkv_workspace_bytes", "rkv_advance", "rkv_append",
-    "rkv_roll_rebase", "rkv_compact", "rkv_decode_attn", "rkv_decode_step",
+    "rkv_roll_rebase", "rkv_update_step", "rkv_compact", "rkv_decode_attn", "rkv_decode_step",
     "rkv_decode_step_pipelined",
     "rkv_encoder_chunk_attn", "rkv_reset_streams", "rkv_restart_step",
     "rkv_mel_filters_host", "rkv_mel_step",
@@ -157,6 +157,7 @@ def lib():
             "rkv_advance": ([pc, vp, vp, vp], ctypes.c_int),
             "rkv_append": ([pc, vp, pk, vp, vp, vp], ctypes.c_int),
             "rkv_roll_rebase": ([pc, vp, pk, vp], ctypes.c_int),
+            "rkv_update_step": ([pc, vp, pk, vp, vp, vp], ctypes.c_int),
             "rkv_compact": ([pc, vp, pk, vp], ctypes.c_int),
             "rkv_decode_attn": ([pc, vp, pk, vp, vp, vp, sz, vp], ctypes.c_int),
             "rkv_decode_step": ([pc, vp, pk, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
@@ -430,6 +431,11 @@ def rkv_workspace_bytes(cfg, slots) -> int:
 def rkv_advance(cfg, state, plan, stream=None):
     _check("rkv_advance", lib().rkv_advance(ctypes.byref(cfg), _ptr(state), _ptr(plan),
                                             _stream(stream)))
+
+
+def rkv_update_step(cfg, plan, kv, k_new, v_new, stream=None):
+    _check("rkv_update_step", lib().rkv_update_step(ctypes.byref(cfg), _ptr(plan), ctypes.byref(kv),
+                                                    _ptr(k_new), _ptr(v_new), _stream(stream)))
 
 
 def rkv_append(cfg, plan, kv, k_new, v_new, stream=None):

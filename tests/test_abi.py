@@ -160,6 +160,10 @@ def test_calls_reject_bad_arguments_without_a_device(rkv):
     assert call(rkv, "rkv_append", c, F, ctypes.byref(kv), N, F, N) == rkv.RKV_EINVAL
     assert call(rkv, "rkv_append", c, F, ctypes.byref(kv), M, F, N) == rkv.RKV_EALIGN
     assert call(rkv, "rkv_append", c, F, N, F, F, N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_update_step", c, F, ctypes.byref(kv), N, F, N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_update_step", c, F, ctypes.byref(kv), F, M, N) == rkv.RKV_EALIGN
+    assert call(rkv, "rkv_update_step", c, N, ctypes.byref(kv), F, F, N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_update_step", c, F, N, F, F, N) == rkv.RKV_EINVAL
     bad_stride = fake_view(rkv, slot_stride=100)
     assert call(rkv, "rkv_roll_rebase", c, F, ctypes.byref(bad_stride), N) == rkv.RKV_EINVAL
     odd_stride = fake_view(rkv, slot_stride=132)

@@ -179,3 +179,64 @@ def test_fused_step_writes_same_bits_as_separate_calls(dc, comp):
                 assert torch.equal(a.k_lo, b.k_lo)
             assert torch.equal(oa, ob_)
     say(f"fused == separate, dc={dc} comp={comp}: rings and outputs bit-identical")
+
+
+@pytest.mark.parametrize("case", ["rebase_dc1_comp", "rebase_dc4", "rebase_fp16_comp",
+                                  "encoder", "compact", "many_streams"])
+def test_update_step_writes_same_bits_as_rebase_then_append(case):
+    """rkv_update_step (one launch) against rkv_roll_rebase + rkv_append (and
+    rkv_compact first in compaction mode): rings bit-identical after every
+    step, with staggered stream origins so that some streams re-base in most
+    steps; 8,300 streams take the moving-stream list through two passes."""
+    rkv = rkv_mod()
+    dev = device()
+    gen = torch.Generator().manual_seed(15)
+    L, S, H, d, W, cap, F, steps = 2, 5, 2, 128, 40, 40, 1, 90
+    kw = dict(num_kv_heads=H, head_dim=d)
+    origins = np.array([0, 3, 7, 11, 30], np.int64)
+    if case == "rebase_dc1_comp":
+        cfg = rkv.make_cfg(S, L, rebase_chunk=1, flags=rkv.RKV_F_COMPENSATED, **kw)
+    elif case == "rebase_dc4":
+        cfg = rkv.make_cfg(S, L, rebase_chunk=4, **kw)
+    elif case == "rebase_fp16_comp":
+        cfg = rkv.make_cfg(S, L, rebase_chunk=3,
+                           flags=rkv.RKV_F_COMPENSATED | rkv.RKV_F_KV_FP16, **kw)
+    elif case == "encoder":
+        H, d, F = 4, 64, 4
+        cfg = rkv.make_cfg(S, L, num_q_heads=H, num_kv_heads=H, head_dim=d,
+                           mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F)
+        cap = W + F
+        origins = 0
+    elif case == "compact":
+        cap = 52
+        cfg = rkv.make_cfg(S, L, mode=rkv.RKV_MODE_COMPACT, **kw)
+    else:
+        L, S, H, d, W, cap, steps = 1, 8300, 1, 64, 6, 6, 14
+        cfg = rkv.make_cfg(S, L, num_q_heads=1, num_kv_heads=1, head_dim=d, rebase_chunk=2)
+        origins = np.arange(S, dtype=np.int64) % 7
+    a = rkv.Cache(cfg, cap, W, cap, origins, device=dev)
+    b = rkv.Cache(cfg, cap, W, cap, origins, device=dev)
+    shape = (L, S, F, H, d) if F > 1 else (L, S, H, d)
+    ks = [_rand_bf16(shape, gen).to(dev) for _ in range(3)]
+    vs = [_rand_bf16(shape, gen).to(dev) for _ in range(3)]
+    moved = 0
+    for step in range(steps):
+        i = step % 3
+        for c in (a, b):
+            rkv.rkv_advance(cfg, c.state, c.plan)
+            if case == "compact":
+                rkv.rkv_compact(cfg, c.plan, c.kv)
+        if step % 7 == 0:
+            moved += int((a.plan_host()["rebase_delta"] != 0).sum())
+        if cfg.mode == rkv.RKV_MODE_REBASE:
+            rkv.rkv_roll_rebase(cfg, a.plan, a.kv)
+        rkv.rkv_append(cfg, a.plan, a.kv, ks[i], vs[i])
+        rkv.rkv_update_step(cfg, b.plan, b.kv, ks[i], vs[i])
+        if step % 5 == 4 or step == steps - 1:
+            torch.cuda.synchronize()
+            assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v), step
+            if a.k_lo is not None:
+                assert torch.equal(a.k_lo, b.k_lo), step
+    if cfg.mode == rkv.RKV_MODE_REBASE:
+        assert moved > 0
+    say(f"update step == re-base + append ({case}): rings bit-identical over {steps} steps")
