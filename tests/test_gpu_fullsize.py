@@ -1,9 +1,11 @@
 """Full-size workloads in the launch configuration bench.py times (one
 rkv_decode_step_pipelined launch per step over all layers, plans alternating
-between two buffers; rkv_encoder_chunk_attn for the encoder; the same input
-pools), checked on sampled (layer, stream) outputs that the oracle computes
-one by one, plus properties that hold at any size (every plan bit-exact
-against the oracle schedule, all outputs finite)."""
+between two buffers; for the mixed-window workload also its default update
+path, rkv_advance + rkv_update_step + rkv_decode_attn; rkv_encoder_chunk_attn
+for the encoder; the same input pools), checked on sampled (layer, stream)
+outputs that the oracle computes one by one, plus properties that hold at any
+size (every plan bit-exact against the oracle schedule, all outputs
+finite)."""
 import numpy as np
 import pytest
 import torch
@@ -40,27 +42,39 @@ def _check_plans(rkv, got, mode, windows, caps, origins, steps, dc=1, F=1):
             assert int(got[f][s]) == getattr(ref, f), (s, f)
 
 
-def _run_decoder_bench(rkv, cfg, slots, windows, caps, origins, q, k, v, steps, keep=()):
-    """The bench's step: rkv_advance primes the first plan, then one pipelined
-    launch per step (after rkv_compact in compaction mode).  Returns the
+def _run_decoder_bench(rkv, cfg, slots, windows, caps, origins, q, k, v, steps, keep=(),
+                       path="pipelined"):
+    """The bench's step.  pipelined: rkv_advance primes the first plan, then one
+    pipelined launch per step (after rkv_compact in compaction mode); update:
+    rkv_advance + rkv_update_step + rkv_decode_attn per step.  Returns the
     cache, the last output, kept outputs and the last step's plans."""
     dev = q.device
     P = q.shape[0]
     cache = rkv.Cache(cfg, slots, windows, caps, origins, device=dev, zero=False)
     out = torch.empty(q.shape[1:], dtype=torch.bfloat16, device=dev)
     plans = [cache.plan, cache.plan_next]
-    rkv.rkv_advance(cfg, cache.state, plans[0])
+    if path == "pipelined":
+        rkv.rkv_advance(cfg, cache.state, plans[0])
     kept = {}
     for t in range(steps):
-        cur, nxt = plans[t % 2], plans[(t + 1) % 2]
-        if cfg.mode == rkv.RKV_MODE_COMPACT:
-            rkv.rkv_compact(cfg, cur, cache.kv)
-        rkv.rkv_decode_step_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[t % P], k[t % P],
-                                      v[t % P], out, cache.workspace)
+        j = t % P
+        if path == "update":
+            rkv.rkv_advance(cfg, cache.state, cache.plan)
+            if cfg.mode == rkv.RKV_MODE_COMPACT:
+                rkv.rkv_compact(cfg, cache.plan, cache.kv)
+            rkv.rkv_update_step(cfg, cache.plan, cache.kv, k[j], v[j])
+            rkv.rkv_decode_attn(cfg, cache.plan, cache.kv, q[j], out, cache.workspace)
+        else:
+            cur, nxt = plans[t % 2], plans[(t + 1) % 2]
+            if cfg.mode == rkv.RKV_MODE_COMPACT:
+                rkv.rkv_compact(cfg, cur, cache.kv)
+            rkv.rkv_decode_step_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[j], k[j], v[j],
+                                          out, cache.workspace)
         if t in keep:
             kept[t] = out.clone()
     torch.cuda.synchronize()
-    last = plans[(steps - 1) % 2].cpu().numpy().view(rkv.PLAN_DTYPE)
+    last_plan = cache.plan if path == "update" else plans[(steps - 1) % 2]
+    last = last_plan.cpu().numpy().view(rkv.PLAN_DTYPE)
     return cache, out, kept, last
 
 
@@ -91,7 +105,8 @@ def test_decode_36_layers_64_streams_w375(fp16):
                         ulp_slack=True)
 
 
-def test_decode_mixed_clocks_256_streams_outliers():
+@pytest.mark.parametrize("path", ["update", "pipelined"])
+def test_decode_mixed_clocks_256_streams_outliers(path):
     rkv = rkv_mod()
     dev = device()
     L, S, dc, P, seed = 36, 256, 25, 16, 1003
@@ -101,9 +116,9 @@ def test_decode_mixed_clocks_256_streams_outliers():
     steps = 375 + 60
     q, k, v = synth.decoder_pool(seed, L, S, P, HQ, HKV, D, 0.01)
     cfg = rkv.make_cfg(S, L, rebase_chunk=dc)
-    say("case: 36x256 mixed W, offsets, outliers")
+    say(f"case: 36x256 mixed W, offsets, outliers, {path} path")
     cache, out, _, last = _run_decoder_bench(rkv, cfg, 375, windows, windows, origins,
-                                             q.to(dev), k.to(dev), v.to(dev), steps)
+                                             q.to(dev), k.to(dev), v.to(dev), steps, path=path)
     assert torch.isfinite(out.float()).all()
     _check_plans(rkv, last, sch.MODE_REBASE, windows, windows, origins, steps, dc)
     got = f64(out)
