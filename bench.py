@@ -251,7 +251,7 @@ def run_gpu(c, args):
     ws = cache.workspace
     separate = args.path in ("separate", "update")
 
-    pipelined = args.path == "pipelined" and c["mode"] != "enc"
+    pipelined = args.path in ("pipelined", "update") and c["mode"] != "enc"
     plans = [cache.plan, cache.plan_next]
     tcond = None
     if args.tcond:
@@ -279,8 +279,13 @@ def run_gpu(c, args):
                 rkv.rkv_compact(cfg, cur, cache.kv, sp)
             if ev is not None:
                 ev[0].record(stream)
-            rkv.rkv_decode_step_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[j], k[j],
-                                          v[j], out, ws, sp)
+            if args.path == "update":
+                rkv.rkv_update_step(cfg, cur, cache.kv, k[j], v[j], sp)
+                rkv.rkv_decode_attn_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[j], out,
+                                              ws, sp)
+            else:
+                rkv.rkv_decode_step_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[j], k[j],
+                                              v[j], out, ws, sp)
             if ev is not None:
                 ev[1].record(stream)
             if tcond is not None:
@@ -293,9 +298,6 @@ def run_gpu(c, args):
             ev[0].record(stream)
         if c["mode"] == "enc":
             rkv.rkv_encoder_chunk_attn(cfg, cache.plan, cache.kv, q[j], k[j], v[j], out, ws, sp)
-        elif args.path == "update":
-            rkv.rkv_update_step(cfg, cache.plan, cache.kv, k[j], v[j], sp)
-            rkv.rkv_decode_attn(cfg, cache.plan, cache.kv, q[j], out, ws, sp)
         elif separate:
             if c["mode"] == "rebase":
                 rkv.rkv_roll_rebase(cfg, cache.plan, cache.kv, sp)
@@ -344,7 +346,8 @@ def run_gpu(c, args):
     # the attention launch of every RUN-th step.
     K = args.steps
     RUN, GAP = 8, 4
-    bracket = pipelined and c["mode"] == "rebase" and K >= RUN and tcond is None
+    bracket = (pipelined and args.path == "pipelined" and c["mode"] == "rebase" and K >= RUN
+               and tcond is None)
     ev_runs, ev_steps = {}, {}
     if args.kernel_events:
         for n in (range(0, K - RUN + 1, RUN * GAP) if bracket else range(0, K, RUN)):
@@ -560,10 +563,10 @@ def main():
                          "pipelined: rkv_decode_step_pipelined (the step plan of the next "
                          "step computed in the same launch); fused: rkv_advance + "
                          "rkv_decode_step; separate: rkv_advance + rkv_roll_rebase + "
-                         "rkv_append + rkv_decode_attn; update: rkv_advance + "
-                         "rkv_update_step (re-base and append in one launch) + "
-                         "rkv_decode_attn (encoder workloads: always rkv_advance + "
-                         "rkv_encoder_chunk_attn)")
+                         "rkv_append + rkv_decode_attn; update: rkv_update_step (re-base and "
+                         "append in one launch) + rkv_decode_attn_pipelined (the read-only "
+                         "attention with the next step's plan in the same launch) (encoder "
+                         "workloads: always rkv_advance + rkv_encoder_chunk_attn)")
     ap.add_argument("--no-kernel-events", dest="kernel_events", action="store_false")
     ap.add_argument("--mel", type=int, default=0, metavar="STREAMS",
                     help="time the rolling log-mel front end for STREAMS streams instead")

@@ -276,6 +276,22 @@ int rkv_decode_step_pipelined(const rkv_cfg* cfg, rkv_stream_state* d_state,
                               const void* v_new, void* out, void* workspace,
                               size_t workspace_bytes, void* hip_stream);
 
+/* Pipelined read-only attention: rkv_decode_attn with d_plan, and in the same
+ * launch the next step's plan written to d_plan_next with d_state advanced,
+ * exactly as in rkv_decode_step_pipelined.  For the update path
+ *   rkv_advance(state, A);
+ *   rkv_update_step(A); attn_pipelined(state, A, B);
+ *   rkv_update_step(B); attn_pipelined(state, B, A); ...
+ * which gives the same rings, outputs, states and plans as rkv_advance +
+ * rkv_update_step + rkv_decode_attn per step in two launches instead of
+ * three.  REBASE and COMPACT modes (COMPACT: rkv_compact with the step's plan
+ * before rkv_update_step); alignment and overlap rules as
+ * rkv_decode_step_pipelined. */
+int rkv_decode_attn_pipelined(const rkv_cfg* cfg, rkv_stream_state* d_state,
+                              const rkv_step_plan* d_plan, rkv_step_plan* d_plan_next,
+                              const rkv_kv_view* kv, const void* q, void* out,
+                              void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Encoder chunk attention (voxtral.c explainer section 三: only the new
  * positions are computed, against the cached K/V of the window).  Appends the
  * F frames of the chunk (as rkv_append) and computes, for every head and frame

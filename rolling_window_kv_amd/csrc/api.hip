@@ -402,6 +402,15 @@ int rkv_decode_step_pipelined(const rkv_cfg* cfg, rkv_stream_state* d_state,
                    workspace_bytes, hip_stream, d_state, d_plan_next);
 }
 
+int rkv_decode_attn_pipelined(const rkv_cfg* cfg, rkv_stream_state* d_state,
+                              const rkv_step_plan* d_plan, rkv_step_plan* d_plan_next,
+                              const rkv_kv_view* kv, const void* q, void* out, void* workspace,
+                              size_t workspace_bytes, void* hip_stream) {
+  if (cfg && cfg->mode == RKV_MODE_ENC_CHUNK) return RKV_EINVAL;
+  return attention(cfg, rkv::kDecodeRead, d_plan, kv, q, nullptr, nullptr, out, workspace,
+                   workspace_bytes, hip_stream, d_state, d_plan_next);
+}
+
 static int check_encoder(const rkv_cfg* cfg, const rkv_encoder_cfg* ec) {
   int rc = check_cfg(cfg);
   if (rc) return rc;

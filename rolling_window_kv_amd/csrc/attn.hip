@@ -161,7 +161,7 @@ void attn_kernel(AttnArgs a) {
 
   // Pipelined decode step: the blocks past the attention grid compute the
   // next step's plan, one wave per stream (nothing in this launch reads it).
-  if (KIND == kDecodeFused && a.adv_state) {
+  if ((KIND == kDecodeFused || KIND == kDecodeRead) && a.adv_state) {
     const int njobs = a.L * a.S * a.Hkv * a.nsplit;
     if ((int)blockIdx.x >= njobs) {
       const int s = ((int)blockIdx.x - njobs) * NW + (int)(threadIdx.x >> 6);

@@ -39,7 +39,7 @@ ENTRY_POINTS = (
     "rkv_version", "rkv_strerror", "rkv_last_hip_error", "rkv_validate_cfg",
     "rkv_state_init_host", "rkv_state_init", "rkv_workspace_bytes", "rkv_advance", "rkv_append",
     "rkv_roll_rebase", "rkv_update_step", "rkv_compact", "rkv_decode_attn", "rkv_decode_step",
-    "rkv_decode_step_pipelined",
+    "rkv_decode_step_pipelined", "rkv_decode_attn_pipelined",
     "rkv_encoder_chunk_attn", "rkv_reset_streams", "rkv_restart_step",
     "rkv_mel_filters_host", "rkv_mel_step",
     "rkv_encoder_layer_weight_bytes", "rkv_encoder_step_workspace_bytes", "rkv_encoder_step",
@@ -162,6 +162,8 @@ def lib():
             "rkv_decode_attn": ([pc, vp, pk, vp, vp, vp, sz, vp], ctypes.c_int),
             "rkv_decode_step": ([pc, vp, pk, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "rkv_decode_step_pipelined": ([pc, vp, vp, vp, pk, vp, vp, vp, vp, vp, sz, vp],
+                                          ctypes.c_int),
+            "rkv_decode_attn_pipelined": ([pc, vp, vp, vp, pk, vp, vp, vp, sz, vp],
                                           ctypes.c_int),
             "rkv_encoder_chunk_attn": ([pc, vp, pk, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "rkv_reset_streams": ([pc, vp, vp, i32, vp, vp, vp], ctypes.c_int),
@@ -472,6 +474,17 @@ def rkv_decode_step(cfg, plan, kv, q, k_new, v_new, out, workspace=None, stream=
                                                     ctypes.byref(kv), _ptr(q), _ptr(k_new),
                                                     _ptr(v_new), _ptr(out), wp, wb,
                                                     _stream(stream)))
+
+
+def rkv_decode_attn_pipelined(cfg, state, plan, plan_next, kv, q, out, workspace=None,
+                              stream=None):
+    """rkv_decode_attn with `plan`, and the next step's plan into `plan_next`
+    (state advanced) in the same launch."""
+    wp, wb = _ws(workspace)
+    _check("rkv_decode_attn_pipelined",
+           lib().rkv_decode_attn_pipelined(ctypes.byref(cfg), _ptr(state), _ptr(plan),
+                                           _ptr(plan_next), ctypes.byref(kv), _ptr(q), _ptr(out),
+                                           wp, wb, _stream(stream)))
 
 
 def rkv_decode_step_pipelined(cfg, state, plan, plan_next, kv, q, k_new, v_new, out,

@@ -164,6 +164,18 @@ def test_calls_reject_bad_arguments_without_a_device(rkv):
     assert call(rkv, "rkv_update_step", c, F, ctypes.byref(kv), F, M, N) == rkv.RKV_EALIGN
     assert call(rkv, "rkv_update_step", c, N, ctypes.byref(kv), F, F, N) == rkv.RKV_EINVAL
     assert call(rkv, "rkv_update_step", c, F, N, F, F, N) == rkv.RKV_EINVAL
+    # read-only pipelined attention: distinct plan buffers, no encoder mode
+    PL2 = ctypes.c_void_p(FAKE + 0x100000)
+    assert call(rkv, "rkv_decode_attn_pipelined", c, F, F, F, ctypes.byref(kv), F, F, N, 0,
+                N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_decode_attn_pipelined", c, N, F, PL2, ctypes.byref(kv), F, F, N, 0,
+                N) == rkv.RKV_EINVAL
+    assert call(rkv, "rkv_decode_attn_pipelined", c, F, F, PL2, ctypes.byref(kv), M, F, N, 0,
+                N) == rkv.RKV_EALIGN
+    enc = rkv.make_cfg(2, 1, num_q_heads=4, num_kv_heads=4, head_dim=64,
+                       mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=4)
+    assert call(rkv, "rkv_decode_attn_pipelined", ctypes.byref(enc), F, F, PL2,
+                ctypes.byref(kv), F, F, N, 0, N) == rkv.RKV_EINVAL
     bad_stride = fake_view(rkv, slot_stride=100)
     assert call(rkv, "rkv_roll_rebase", c, F, ctypes.byref(bad_stride), N) == rkv.RKV_EINVAL
     odd_stride = fake_view(rkv, slot_stride=132)

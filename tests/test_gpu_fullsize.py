@@ -1,7 +1,7 @@
 """Full-size workloads in the launch configuration bench.py times (one
 rkv_decode_step_pipelined launch per step over all layers, plans alternating
 between two buffers; for the mixed-window workload also its default update
-path, rkv_advance + rkv_update_step + rkv_decode_attn; rkv_encoder_chunk_attn
+path, rkv_update_step + rkv_decode_attn_pipelined; rkv_encoder_chunk_attn
 for the encoder; the same input pools), checked on sampled (layer, stream)
 outputs that the oracle computes one by one, plus properties that hold at any
 size (every plan bit-exact against the oracle schedule, all outputs
@@ -44,37 +44,34 @@ def _check_plans(rkv, got, mode, windows, caps, origins, steps, dc=1, F=1):
 
 def _run_decoder_bench(rkv, cfg, slots, windows, caps, origins, q, k, v, steps, keep=(),
                        path="pipelined"):
-    """The bench's step.  pipelined: rkv_advance primes the first plan, then one
-    pipelined launch per step (after rkv_compact in compaction mode); update:
-    rkv_advance + rkv_update_step + rkv_decode_attn per step.  Returns the
-    cache, the last output, kept outputs and the last step's plans."""
+    """The bench's step: rkv_advance primes the first plan, then per step (after
+    rkv_compact in compaction mode) one pipelined launch (pipelined), or
+    rkv_update_step + rkv_decode_attn_pipelined (update), plans alternating
+    between two buffers.  Returns the cache, the last output, kept outputs
+    and the last step's plans."""
     dev = q.device
     P = q.shape[0]
     cache = rkv.Cache(cfg, slots, windows, caps, origins, device=dev, zero=False)
     out = torch.empty(q.shape[1:], dtype=torch.bfloat16, device=dev)
     plans = [cache.plan, cache.plan_next]
-    if path == "pipelined":
-        rkv.rkv_advance(cfg, cache.state, plans[0])
+    rkv.rkv_advance(cfg, cache.state, plans[0])
     kept = {}
     for t in range(steps):
         j = t % P
+        cur, nxt = plans[t % 2], plans[(t + 1) % 2]
+        if cfg.mode == rkv.RKV_MODE_COMPACT:
+            rkv.rkv_compact(cfg, cur, cache.kv)
         if path == "update":
-            rkv.rkv_advance(cfg, cache.state, cache.plan)
-            if cfg.mode == rkv.RKV_MODE_COMPACT:
-                rkv.rkv_compact(cfg, cache.plan, cache.kv)
-            rkv.rkv_update_step(cfg, cache.plan, cache.kv, k[j], v[j])
-            rkv.rkv_decode_attn(cfg, cache.plan, cache.kv, q[j], out, cache.workspace)
+            rkv.rkv_update_step(cfg, cur, cache.kv, k[j], v[j])
+            rkv.rkv_decode_attn_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[j], out,
+                                          cache.workspace)
         else:
-            cur, nxt = plans[t % 2], plans[(t + 1) % 2]
-            if cfg.mode == rkv.RKV_MODE_COMPACT:
-                rkv.rkv_compact(cfg, cur, cache.kv)
             rkv.rkv_decode_step_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[j], k[j], v[j],
                                           out, cache.workspace)
         if t in keep:
             kept[t] = out.clone()
     torch.cuda.synchronize()
-    last_plan = cache.plan if path == "update" else plans[(steps - 1) % 2]
-    last = last_plan.cpu().numpy().view(rkv.PLAN_DTYPE)
+    last = plans[(steps - 1) % 2].cpu().numpy().view(rkv.PLAN_DTYPE)
     return cache, out, kept, last
 
 

@@ -1,7 +1,8 @@
-"""rkv_decode_step_pipelined against rkv_advance + rkv_decode_step: the same
-outputs, rings, states and plans, bit for bit, when the caller alternates two
-plan buffers (re-base steps, compaction steps, a split key range and a stream
-count that leaves part of the last plan block idle)."""
+"""rkv_decode_step_pipelined, and rkv_update_step + rkv_decode_attn_pipelined,
+against rkv_advance + rkv_decode_step: the same outputs, rings, states and
+plans, bit for bit, when the caller alternates two plan buffers (re-base
+steps, compaction steps, a split key range and a stream count that leaves
+part of the last plan block idle)."""
 import numpy as np
 import pytest
 import torch
@@ -18,15 +19,16 @@ def _pair(rkv, cfg, slots, W, cap, origins, dev):
     return [rkv.Cache(cfg, slots, W, cap, origins, device=dev) for _ in range(2)]
 
 
+@pytest.mark.parametrize("path", ["fused", "update"])
 @pytest.mark.parametrize("mode,S,L,W,cap,dc,steps", [
     (0, 5, 2, 40, 40, 5, 130),        # re-base every 5 positions once the window is full
     (1, 3, 2, 24, 30, 1, 90),         # compaction every 7 steps after the first fill
     (0, 1, 1, 375, 375, 25, 420),     # one item: the key range is split
 ])
-def test_pipelined_step_matches_advance_then_step(mode, S, L, W, cap, dc, steps):
+def test_pipelined_step_matches_advance_then_step(mode, S, L, W, cap, dc, steps, path):
     rkv = rkv_mod()
     dev = device()
-    say(f"pipelined: mode={mode} S={S} L={L} W={W} cap={cap} dc={dc} steps={steps}")
+    say(f"pipelined ({path}): mode={mode} S={S} L={L} W={W} cap={cap} dc={dc} steps={steps}")
     cfg = rkv.make_cfg(S, L, mode=mode, rebase_chunk=dc)
     origins = np.arange(S, dtype=np.int64) * 3
     a, b = _pair(rkv, cfg, cap, W, cap, origins, dev)
@@ -48,8 +50,12 @@ def test_pipelined_step_matches_advance_then_step(mode, S, L, W, cap, dc, steps)
             rkv.rkv_compact(cfg, a.plan, a.kv)
             rkv.rkv_compact(cfg, cur, b.kv)
         rkv.rkv_decode_step(cfg, a.plan, a.kv, q[j], k[j], v[j], oa, a.workspace)
-        rkv.rkv_decode_step_pipelined(cfg, b.state, cur, nxt, b.kv, q[j], k[j], v[j], ob,
-                                      b.workspace)
+        if path == "update":
+            rkv.rkv_update_step(cfg, cur, b.kv, k[j], v[j])
+            rkv.rkv_decode_attn_pipelined(cfg, b.state, cur, nxt, b.kv, q[j], ob, b.workspace)
+        else:
+            rkv.rkv_decode_step_pipelined(cfg, b.state, cur, nxt, b.kv, q[j], k[j], v[j], ob,
+                                          b.workspace)
         pa = a.plan_host()
         rebases += int((pa["rebase_delta"] != 0).sum())
         drops += int((pa["compact_drop"] != 0).sum())
