@@ -48,11 +48,14 @@ def _cfg(rkv, L, S, H, d, F):
                         mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F)
 
 
-def test_small_stack_wraps_the_ring():
-    """3 layers, 3 streams x 4 frames = 12 tokens (a ragged tile), hidden 256,
-    window 20 frames in a 24-slot ring: 12 steps wrap it twice."""
+@pytest.mark.parametrize("L,S,H,ffn,steps", [(3, 3, 4, 1024, 12), (2, 3, 5, 640, 8)])
+def test_small_stack_wraps_the_ring(L, S, H, ffn, steps):
+    """3 streams x 4 frames = 12 tokens (a ragged tile), window 20 frames in a
+    24-slot ring, enough steps to wrap it; hidden 256 / MLP 1024 (both residual
+    products in four k-slices) and hidden 320 / MLP 640 (the output projection
+    in one slice, the MLP's second product in two)."""
     rkv = rkv_mod()
-    L, S, H, d, F, W, ffn, steps = 3, 3, 4, 64, 4, 20, 1024, 12
+    d, F, W = 64, 4, 20
     dev, ecfg, layers, xin, wts = _setup(rkv, L, S, H, d, F, W, ffn, 77, steps)
     cfg = _cfg(rkv, L, S, H, d, F)
     cap = W + F
@@ -72,7 +75,8 @@ def test_small_stack_wraps_the_ring():
         ref = oes.EncoderStack(wts, H, d, W, F, 1e6, 1e-5)
         for t in range(steps):
             worst = max(worst, _err(outs[t][s], ref.step(xin[t, s].numpy().astype(np.float64))))
-    say(f"small stack: max |gpu - oracle| / max(1, rms) = {worst:.3e}")
+    say(f"small stack (hidden {H * d}, MLP {ffn}): max |gpu - oracle| / max(1, rms) = "
+        f"{worst:.3e}")
     assert worst < GATE
 
 
