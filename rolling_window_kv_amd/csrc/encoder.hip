@@ -46,7 +46,7 @@ __device__ __forceinline__ float gelu_erf(float x) {
 
 constexpr int kTM = 64, kTN = 64, kKS = 64;
 constexpr int kLdk = kKS + 8;      // LDS row stride (elements): 144 B, rows rotate banks
-constexpr int kDepth = 4;          // k-stages whose global loads are in flight
+constexpr int kDepth = 2;          // k-stages whose global loads are in flight
 
 template <int EP>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmSet set, int M, int N, int K, int ld) {
