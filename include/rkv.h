@@ -99,7 +99,8 @@ typedef struct rkv_cfg {
   int32_t rebase_chunk;  /* REBASE: the base moves in multiples of this (>= 1) */
   int32_t new_rows;      /* rows appended per step: 1, or F (1..8) for ENC_CHUNK */
   uint32_t flags;        /* RKV_F_* */
-  int32_t num_splits;    /* key-range splits per (layer, stream, head); 0 = library choice */
+  int32_t num_splits;    /* key-range splits per (layer, stream, head), at most 64 and one
+                            per 16 slots are used; 0 = library choice */
   double rope_base;      /* > 0, e.g. 1e6 */
   float softmax_scale;   /* 0 = 1/sqrt(d) */
   int32_t reserved;

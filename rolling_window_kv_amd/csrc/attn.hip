@@ -679,36 +679,68 @@ void attn_kernel(AttnArgs a) {
 }
 
 // Merge the split partials of one item: out = sum_j 2^(m_j - M) num_j / sum_j 2^(m_j - M) l_j.
+// One thread per (column, dim) output.  The splits' maxima and sums of one
+// item are staged through LDS once and each column's weights computed once,
+// and a thread issues the loads of all its partial numerators together, so a
+// merge costs about two memory round trips however many splits there are.
+// The sums run over the splits in order, as a plain loop would.
+constexpr int kCombineThreads = 1024;
+constexpr int kMaxSplits = 64;
+
 template <int D, int KIND>
-__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a) {
+  __shared__ float sm_m[kMaxSplits][8];
+  __shared__ float sm_l[kMaxSplits][8];
+  __shared__ float sm_f[kMaxSplits][8];
+  __shared__ float sm_den[8];
   const int item = blockIdx.x;
   const int g = item % a.Hkv;
   const int s = (item / a.Hkv) % a.S;
   const int l = item / (a.Hkv * a.S);
-  const float* base = a.ws + (int64_t)item * a.nsplit * partial_floats(D);
-  const int total = a.G * D;
-  for (int idx = threadIdx.x; idx < total; idx += 256) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float M = -INFINITY;
-    for (int j = 0; j < a.nsplit; ++j) M = fmaxf(M, base[j * partial_floats(D) + h]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      for (int j = 0; j < a.nsplit; ++j) {
-        const float* pp = base + j * partial_floats(D);
-        const float mj = pp[h];
-        const float f = mj == -INFINITY ? 0.f : fast_exp2(mj - M);
-        num += f * pp[16 + h * D + d];
-        den += f * pp[8 + h];
-      }
-    }
-    const float o = den > 0.f ? num / den : 0.f;
-    int64_t off;
-    if (KIND == kEncoderFused) off = ((((int64_t)l * a.S + s) * a.F + h) * a.Hkv + g) * D + d;
-    else off = ((((int64_t)l * a.S + s) * a.Hkv + g) * a.G + h) * D + d;
-    if (a.out_f32) reinterpret_cast<float*>(a.out)[off] = o;
-    else reinterpret_cast<uint16_t*>(a.out)[off] = (uint16_t)f2bf(o);
+  const int ns = a.nsplit;
+  const int64_t pf = partial_floats(D);
+  const float* base = a.ws + (int64_t)item * ns * pf;
+  for (int i = threadIdx.x; i < ns * 8; i += kCombineThreads) {
+    const int j = i >> 3, h = i & 7;
+    sm_m[j][h] = base[j * pf + h];
+    sm_l[j][h] = base[j * pf + 8 + h];
   }
+  __syncthreads();
+  if ((int)threadIdx.x < a.G) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+    for (int j = 0; j < ns; ++j) M = fmaxf(M, sm_m[j][h]);
+    float den = 0.f;
+    for (int j = 0; j < ns; ++j) {
+      const float mj = sm_m[j][h];
+      const float f = (M == -INFINITY || mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
+      sm_f[j][h] = f;
+      den += f * sm_l[j][h];
+    }
+    sm_den[h] = den;
+  }
+  __syncthreads();
+  const int idx = threadIdx.x;
+  if (idx >= a.G * D) return;
+  const int h = idx / D;
+  const int d = idx - h * D;
+  const float* num_p = base + 16 + h * D + d;
+  float num = 0.f;
+  for (int j0 = 0; j0 < ns; j0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = j0 + u < ns ? num_p[(j0 + u) * pf] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < ns) num += sm_f[j0 + u][h] * v[u];
+  }
+  const float den = sm_den[h];
+  const float o = den > 0.f ? num / den : 0.f;
+  int64_t off;
+  if (KIND == kEncoderFused) off = ((((int64_t)l * a.S + s) * a.F + h) * a.Hkv + g) * D + d;
+  else off = ((((int64_t)l * a.S + s) * a.Hkv + g) * a.G + h) * D + d;
+  if (a.out_f32) reinterpret_cast<float*>(a.out)[off] = o;
+  else reinterpret_cast<uint16_t*>(a.out)[off] = (uint16_t)f2bf(o);
 }
 
 constexpr int kWavesPerGroup = 4;
@@ -721,7 +753,8 @@ hipError_t launch_kind(const AttnArgs& args, int items, hipStream_t stream) {
                      args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || args.nsplit == 1) return e;
-  hipLaunchKernelGGL((combine_kernel<D, KIND>), dim3(items), dim3(256), 0, stream, args);
+  hipLaunchKernelGGL((combine_kernel<D, KIND>), dim3(items), dim3(kCombineThreads), 0, stream,
+                     args);
   return hipGetLastError();
 }
 
@@ -747,7 +780,8 @@ hipError_t launch_d(AttnKind kind, bool comp, bool f16, const AttnArgs& args, in
 
 int choose_splits(const rkv_cfg* cfg, int32_t slots) {
   if (cfg->num_splits > 0) {
-    const int max_split = (slots + 15) / 16;
+    int max_split = (slots + 15) / 16;
+    if (max_split > kMaxSplits) max_split = kMaxSplits;
     return cfg->num_splits < max_split ? cfg->num_splits : (max_split > 0 ? max_split : 1);
   }
   const int64_t items = (int64_t)cfg->num_layers * cfg->num_streams * cfg->num_kv_heads;
