@@ -133,11 +133,13 @@ struct VChunk<4> {
 
 constexpr float kLazyMax = 8.0f;  // rescale only when the max grows by > 2^8
 
-// Waves per SIMD the register allocation targets: the largest count that
-// fits without spilling (the compensated re-base keeps two more K arrays live).
+// Waves per SIMD the register allocation targets: 3, the fastest measured for
+// both head sizes (d = 64 would fit 4, which ran ~1 % slower: a fuller
+// memory queue lengthens every load's wait), or 2 where the compensated
+// re-base keeps two more K arrays live at d = 128.
 template <int D, bool COMP>
 struct Occupancy {
-  static constexpr int waves = D == 128 ? (COMP ? 2 : 3) : (COMP ? 3 : 4);
+  static constexpr int waves = D == 128 && COMP ? 2 : 3;
 };
 
 template <int D, int NW, int KIND, bool COMP, typename SF>
