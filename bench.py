@@ -221,7 +221,7 @@ def run_gpu(c, args):
     kv_flags = rkv.RKV_F_KV_FP16 if args.kv_fp16 else 0
     if c["mode"] == "rebase":
         flags = (rkv.RKV_F_COMPENSATED if c.get("comp") else 0) | kv_flags
-        cfg = rkv.make_cfg(S, L, rebase_chunk=c["dc"], flags=flags)
+        cfg = rkv.make_cfg(S, L, rebase_chunk=c["dc"], flags=flags, num_splits=args.splits)
         if isinstance(c["W"], tuple):
             counts = [86, 85, 85]
             windows = np.repeat(np.array(c["W"], np.int32), counts)
@@ -235,7 +235,8 @@ def run_gpu(c, args):
         cache = rkv.Cache(cfg, slots, windows, windows, origins, device=dev, zero=False, layout=args.layout)
         prefill = slots
     elif c["mode"] == "compact":
-        cfg = rkv.make_cfg(S, L, mode=rkv.RKV_MODE_COMPACT, flags=kv_flags)
+        cfg = rkv.make_cfg(S, L, mode=rkv.RKV_MODE_COMPACT, flags=kv_flags,
+                           num_splits=args.splits)
         cache = rkv.Cache(cfg, c["cap"], c["W"], c["cap"], 0, device=dev, zero=False, layout=args.layout)
         prefill = c["cap"]
     else:
@@ -251,8 +252,43 @@ def run_gpu(c, args):
     ws = cache.workspace
     separate = args.path in ("separate", "update")
 
-    pipelined = args.path in ("pipelined", "update") and c["mode"] != "enc"
+    pipelined = (args.path in ("pipelined", "update") and c["mode"] != "enc"
+                 and not args.per_layer)
     plans = [cache.plan, cache.plan_next]
+    per_layer = None
+    if args.per_layer:
+        # one call per layer and step, as a decoder whose layer l + 1 needs
+        # layer l's output would make them; the step plan is shared
+        if c["mode"] == "enc":
+            cfg1 = rkv.make_cfg(S, 1, num_q_heads=c["H"], num_kv_heads=c["H"], head_dim=c["d"],
+                                mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=c["F"])
+        else:
+            cfg1 = rkv.make_cfg(S, 1, mode=cfg.mode, rebase_chunk=cfg.rebase_chunk,
+                                flags=cfg.flags, num_splits=args.splits)
+        views = [rkv.kv_view(cache.k[l:l + 1], cache.v[l:l + 1],
+                             None if cache.k_lo is None else cache.k_lo[l:l + 1])
+                 for l in range(L)]
+        nb = rkv.rkv_workspace_bytes(cfg1, cache.k.shape[3])
+        ws1 = torch.empty((nb + 3) // 4, dtype=torch.float32, device=dev) if nb else None
+        slices = [[(q[j][l], k[j][l], v[j][l]) for l in range(L)] for j in range(q.shape[0])]
+        outs = [out[l] for l in range(L)]
+        per_layer = (cfg1, views, ws1, slices, outs)
+
+    def layer_calls(j, st):
+        """One step in per-layer mode: the plan, then one launch per layer."""
+        cfg1, views, ws1, slices, outs = per_layer
+        rkv.rkv_advance(cfg, cache.state, cache.plan, st)
+        if c["mode"] == "compact":
+            rkv.rkv_compact(cfg, cache.plan, cache.kv, st)
+        for l in range(L):
+            ql, kl, vl = slices[j][l]
+            if c["mode"] == "enc":
+                rkv.rkv_encoder_chunk_attn(cfg1, cache.plan, views[l], ql, kl, vl, outs[l], ws1,
+                                           st)
+            else:
+                rkv.rkv_decode_step(cfg1, cache.plan, views[l], ql, kl, vl, outs[l], ws1, st)
+
+    graphs = None
     tcond = None
     if args.tcond:
         # delay conditioning after each step's attention: the 8 post-trained
@@ -271,6 +307,12 @@ def run_gpu(c, args):
 
     def step(i, ev=None):
         j = i % P
+        if per_layer is not None:
+            if graphs is not None:
+                graphs[j].replay()
+            else:
+                layer_calls(j, sp)
+            return
         if pipelined:
             # one launch per step: this step's plan was written by the previous
             # launch (or the priming rkv_advance), the next one is written now
@@ -331,6 +373,17 @@ def run_gpu(c, args):
         i += 1
     if pipelined:                     # the first pipelined step's plan
         rkv.rkv_advance(cfg, cache.state, plans[i % 2], sp)
+    if per_layer is not None and args.graph:
+        # one HIP graph per pool entry (the inputs differ), each the whole
+        # step: the plan and the L per-layer launches.  Capturing runs nothing.
+        torch.cuda.synchronize()
+        graphs = []
+        for j in range(P):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layer_calls(j, None)
+            graphs.append(g)
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(i)
         i += 1
@@ -348,6 +401,8 @@ def run_gpu(c, args):
     RUN, GAP = 8, 4
     bracket = (pipelined and args.path == "pipelined" and c["mode"] == "rebase" and K >= RUN
                and tcond is None)
+    if per_layer is not None:
+        args.kernel_events = False    # the roofline uses the whole step's time
     ev_runs, ev_steps = {}, {}
     if args.kernel_events:
         for n in (range(0, K - RUN + 1, RUN * GAP) if bracket else range(0, K, RUN)):
@@ -573,6 +628,16 @@ def main():
     ap.add_argument("--encoder-stack", type=int, default=0, metavar="STREAMS",
                     help="time the 32-layer incremental encoder step for STREAMS streams "
                          "instead")
+    ap.add_argument("--per-layer", action="store_true",
+                    help="one launch per layer and step (rkv_decode_step or "
+                         "rkv_encoder_chunk_attn with a one-layer view of the cache, after "
+                         "one rkv_advance), as a decoder whose layers run in sequence calls "
+                         "them")
+    ap.add_argument("--splits", type=int, default=0, metavar="N",
+                    help="key-range splits per (layer, stream, head) of the attention "
+                         "launches (0: the library's choice)")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --per-layer: replay each step as a captured HIP graph")
     ap.add_argument("--layout", choices=("interleaved", "separate"), default="interleaved",
                     help="ring layout: K and V rows of a slot side by side (interleaved) or "
                          "K and V in separate buffers")
@@ -617,13 +682,20 @@ def main():
         print(json.dumps(run_encoder_stack(args)), flush=True)
         return
     c = dict(CONFIGS[args.config])
+    if args.graph and not args.per_layer:
+        print("--graph applies to --per-layer", file=sys.stderr)
+        sys.exit(2)
+    if args.per_layer and (args.tcond or args.path not in (None, "fused")):
+        print("--per-layer runs rkv_advance + one fused step per layer", file=sys.stderr)
+        sys.exit(2)
     if args.tcond and c["mode"] == "enc":
         print("--tcond: delay conditioning applies to the decoder workloads", file=sys.stderr)
         sys.exit(2)
     if args.kv_fp16 and c["mode"] == "enc":
         print("--kv-fp16: the encoder cache is bfloat16 only", file=sys.stderr)
         sys.exit(2)
-    args.path = c.get("path", "pipelined") if args.path is None else args.path
+    if args.path is None:
+        args.path = "fused" if args.per_layer else c.get("path", "pipelined")
     args.steps = c["steps"] if args.steps is None else args.steps
     args.warmup = c["warmup"] if args.warmup is None else args.warmup
 
@@ -656,6 +728,15 @@ def main():
                     "kernel_launches_timed": r["kernel_samples"],
                     "kernel_timing": r["kernel_timing"],
                     "alg_bytes_per_launch": per_launch}
+    if args.per_layer:
+        # L launches per step: the roofline takes the whole step's time
+        roofline = {"bound": "hbm", "achieved": round(step_gbps, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(step_gbps / PEAK_HBM_GBPS, 4),
+                    "traffic": None,
+                    "kernel": f"{L} per-layer launches per step ({kernel})",
+                    "kernel_ms": round(r["elapsed_ms"] / K, 5),
+                    "kernel_timing": "whole step (HIP events around the timed steps)",
+                    "alg_bytes_per_step": b_sl * L * S}
     res = {
         "metric": METRIC,
         "value": round(sl_steps, 1),
@@ -670,7 +751,8 @@ def main():
         "dtype": "fp16 cache, bf16 i/o" if args.kv_fp16 else "bf16",
         "data": "synthetic",
         "config": {"workload": c["name"], "layers": L, "streams": S,
-                   "path": args.path if c["mode"] != "enc" else "fused",
+                   "path": ("per-layer" + (" graph" if args.graph else "")) if args.per_layer
+                           else (args.path if c["mode"] != "enc" else "fused"),
                    "alg_bytes_per_stream_layer_step": b_sl,
                    **({"layout": args.layout} if args.layout != "interleaved" else {}),
                    **({"tcond": "rkv_tcond_modulate after each step, 8 settings, dim 256"}
@@ -681,7 +763,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if args.cpu and not args.kv_fp16 and not args.tcond:
+    if args.cpu and not args.kv_fp16 and not args.tcond and not args.per_layer:
         res["cpu_baseline"] = cpu_baseline(c, 1000 + args.config, args.cpu_budget)
     print(json.dumps(res), flush=True)
 

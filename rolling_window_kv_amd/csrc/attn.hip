@@ -786,12 +786,19 @@ int choose_splits(const rkv_cfg* cfg, int32_t slots) {
     if (max_split > kMaxSplits) max_split = kMaxSplits;
     return cfg->num_splits < max_split ? cfg->num_splits : (max_split > 0 ? max_split : 1);
   }
+  // Enough workgroups to spread a small launch over the chip (about 2048),
+  // but no split shorter than 256 keys: a short split's fixed costs and the
+  // merge launch cost more than its parallelism gains (measured: one split
+  // is fastest at W = 375 for any item count, six help at W = 2048 up to 32
+  // items).  Re-basing every position with the residual costs several times
+  // more per key, so there splits of 64 keys still pay.
   const int64_t items = (int64_t)cfg->num_layers * cfg->num_streams * cfg->num_kv_heads;
   const int64_t target = 2048;
   int64_t n = (target + items - 1) / items;
-  const int64_t max_split = (slots + 63) / 64;
+  const bool heavy = (cfg->flags & RKV_F_COMPENSATED) && cfg->rebase_chunk == 1;
+  const int64_t max_split = slots / (heavy ? 64 : 256);
   if (n > max_split) n = max_split;
-  if (n > 64) n = 64;
+  if (n > kMaxSplits) n = kMaxSplits;
   if (n < 1) n = 1;
   return (int)n;
 }

@@ -129,9 +129,19 @@ def test_state_init_rejects_inconsistent_streams(rkv):
 def test_workspace_sizes(rkv):
     # 36 x 64 x 2 = 4608 items: no split needed
     assert rkv.rkv_workspace_bytes(good_cfg(rkv, num_streams=64, num_layers=36), 375) == 0
-    # one stream, one layer: split into ceil(375/64) = 6 ranges
-    ws = rkv.rkv_workspace_bytes(good_cfg(rkv, num_streams=1, num_layers=1, rebase_chunk=1), 375)
-    assert ws == 2 * 6 * (16 + 8 * 128) * 4
+    # one stream, one layer, W = 375: splits of 256 keys at least, so none
+    one = dict(num_streams=1, num_layers=1)
+    assert rkv.rkv_workspace_bytes(good_cfg(rkv, **one), 375) == 0
+    # ... with 2048 keys: 8 ranges (2 items, 2048 / 256 keys each)
+    assert rkv.rkv_workspace_bytes(good_cfg(rkv, **one), 2048) == 2 * 8 * (16 + 8 * 128) * 4
+    # re-base every position with the residual: splits of 64 keys, 375 // 64 = 5
+    comp = good_cfg(rkv, rebase_chunk=1, flags=rkv.RKV_F_COMPENSATED, **one)
+    assert rkv.rkv_workspace_bytes(comp, 375) == 2 * 5 * (16 + 8 * 128) * 4
+    # an explicit count is kept up to one split per 16 slots and 64 in all
+    assert rkv.rkv_workspace_bytes(good_cfg(rkv, num_splits=6, **one), 375) == \
+        2 * 6 * (16 + 8 * 128) * 4
+    assert rkv.rkv_workspace_bytes(good_cfg(rkv, num_splits=100, **one), 8192) == \
+        2 * 64 * (16 + 8 * 128) * 4
     assert rkv.rkv_workspace_bytes(good_cfg(rkv, head_dim=3), 375) == 0
 
 
@@ -192,7 +202,7 @@ def test_calls_reject_bad_arguments_without_a_device(rkv):
     assert call(rkv, "rkv_roll_rebase", ctypes.byref(ccfg), F, ctypes.byref(kv),
                 N) == rkv.RKV_EINVAL
     # decode: missing workspace when the key range is split
-    one = good_cfg(rkv, num_streams=1, num_layers=1)
+    one = good_cfg(rkv, num_streams=1, num_layers=1, num_splits=6)
     assert call(rkv, "rkv_decode_attn", ctypes.byref(one), F, ctypes.byref(kv), F, F, N, 0,
                 N) == rkv.RKV_ESPACE
     assert call(rkv, "rkv_decode_step", ctypes.byref(one), F, ctypes.byref(kv), F, F, F, F,

@@ -23,13 +23,13 @@ def _pair(rkv, cfg, slots, W, cap, origins, dev):
 @pytest.mark.parametrize("mode,S,L,W,cap,dc,steps", [
     (0, 5, 2, 40, 40, 5, 130),        # re-base every 5 positions once the window is full
     (1, 3, 2, 24, 30, 1, 90),         # compaction every 7 steps after the first fill
-    (0, 1, 1, 375, 375, 25, 420),     # one item: the key range is split
+    (0, 1, 1, 375, 375, 25, 420),     # one item, the key range split 6 ways
 ])
 def test_pipelined_step_matches_advance_then_step(mode, S, L, W, cap, dc, steps, path):
     rkv = rkv_mod()
     dev = device()
     say(f"pipelined ({path}): mode={mode} S={S} L={L} W={W} cap={cap} dc={dc} steps={steps}")
-    cfg = rkv.make_cfg(S, L, mode=mode, rebase_chunk=dc)
+    cfg = rkv.make_cfg(S, L, mode=mode, rebase_chunk=dc, num_splits=6 if S == 1 else 0)
     origins = np.arange(S, dtype=np.int64) * 3
     a, b = _pair(rkv, cfg, cap, W, cap, origins, dev)
     gen = torch.Generator().manual_seed(21)
