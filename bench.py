@@ -431,8 +431,9 @@ def run_gpu(c, args):
     elif ev_steps:
         kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_steps.values()]))
         kernel_samples = len(ev_steps)
+    copy_gbps = device_copy_gbps()     # after the timed region
     return dict(cfg=cfg, elapsed_ms=elapsed_ms, kernel_ms=kernel_ms, wall_s=wall,
-                kernel_samples=kernel_samples,
+                kernel_samples=kernel_samples, copy_gbps=copy_gbps,
                 kernel_timing="event pair per run of %d back-to-back launches" % RUN
                 if ev_runs else "event pair around sampled launches",
                 setup_s=setup_s, prefill=prefill)
@@ -553,6 +554,27 @@ def run_encoder_stack(args):
                          "kernel": "rkv_encoder_step (whole step)", "bytes_per_step": nbytes,
                          "matrix_tflops": round(tflops, 2), "flops_per_step": flops},
             "cpu_baseline": None}
+
+
+def device_copy_gbps(mib=1024, reps=10):
+    """Read + write bandwidth of a plain device-to-device copy (torch) on the
+    same GPU: the practical ceiling for traffic that reads and writes."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    gbps = 2 * n * 4 * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return gbps
 
 
 def summarize_rocprof(root, last=0):
@@ -758,6 +780,8 @@ def main():
                    **({"tcond": "rkv_tcond_modulate after each step, 8 settings, dim 256"}
                       if args.tcond else {})},
         "achieved_GBps_step": round(step_gbps, 1),
+        "device_copy_GBps": round(r["copy_gbps"], 1),
+        "frac_of_device_copy": round(step_gbps / r["copy_gbps"], 4),
         "hbm_frac_step": round(step_gbps / PEAK_HBM_GBPS, 4),
         "clock_steps_per_s": round(K / secs, 1),
         "roofline": roofline,
