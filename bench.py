@@ -729,7 +729,7 @@ def main():
     step_gbps = b_sl * L * S * K / secs / 1e9
     kernel = {"rebase": "attn_kernel<128,4,decode_fused>",
               "compact": "attn_kernel<128,4,decode_fused>",
-              "enc": "attn_kernel<64,4,encoder_fused>"}[c["mode"]]
+              "enc": "attn_kernel<64,2,encoder_fused>"}[c["mode"]]
     if args.path == "separate" and c["mode"] != "enc":
         kernel = "rebase+append+attn_kernel<128,4,decode_read>"
     if args.path == "update" and c["mode"] != "enc":

@@ -745,15 +745,29 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a) {
   else reinterpret_cast<uint16_t*>(a.out)[off] = (uint16_t)f2bf(o);
 }
 
-constexpr int kWavesPerGroup = 4;
+// Waves per workgroup (one item each): 4, or 2 at d = 64 when a launch has
+// many items.  Then an item's rows are half as long and the shorter-lived,
+// more numerous workgroups keep the memory queue fuller: the 32-layer
+// encoder launch (81,920 items) runs 5 % faster with 2 (3 and 6 were
+// slower); a one-layer encoder launch (2,560 items, under 2 rounds of
+// resident 2-wave workgroups) is faster with 4, as is every d = 128 case.
+constexpr int64_t kManyItems = 12288;
+
+template <int D, int NW, int KIND, bool COMP, typename SF>
+hipError_t launch_nw(const AttnArgs& args, int items, hipStream_t stream) {
+  const int extra = args.adv_state ? (args.S + NW - 1) / NW : 0;
+  hipLaunchKernelGGL((attn_kernel<D, NW, KIND, COMP, SF>),
+                     dim3(items * args.nsplit + extra), dim3(NW * 64), 0, stream, args);
+  return hipGetLastError();
+}
 
 template <int D, int KIND, bool COMP, typename SF>
 hipError_t launch_kind(const AttnArgs& args, int items, hipStream_t stream) {
-  const int extra = args.adv_state ? (args.S + kWavesPerGroup - 1) / kWavesPerGroup : 0;
-  hipLaunchKernelGGL((attn_kernel<D, kWavesPerGroup, KIND, COMP, SF>),
-                     dim3(items * args.nsplit + extra), dim3(kWavesPerGroup * 64), 0, stream,
-                     args);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (D == 64 && (int64_t)items * args.nsplit >= kManyItems)
+    e = launch_nw<D, 2, KIND, COMP, SF>(args, items, stream);
+  else
+    e = launch_nw<D, 4, KIND, COMP, SF>(args, items, stream);
   if (e != hipSuccess || args.nsplit == 1) return e;
   hipLaunchKernelGGL((combine_kernel<D, KIND>), dim3(items), dim3(kCombineThreads), 0, stream,
                      args);
