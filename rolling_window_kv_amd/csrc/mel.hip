@@ -9,8 +9,8 @@
 // tail ++ new samples, so every frame is causal and a step of n samples
 // yields n / hop frames.  One workgroup per (stream, frame): the windowed
 // frame and a twiddle table sit in LDS, a thread per DFT bin sums the real
-// DFT in float32, and a thread per mel band applies its filter row and the
-// log.  The new tail is the last n_fft - hop new samples (the step carries
+// DFT in float32 (its twiddles by rotation, see below), and a thread per mel
+// band applies its filter row and the log.  The new tail is the last n_fft - hop new samples (the step carries
 // at least that many), written to a second buffer so that no workgroup reads
 // a tail another one has replaced.
 
@@ -24,6 +24,7 @@ namespace rkv {
 namespace {
 
 constexpr int kMelThreads = 256;
+constexpr int kMelResync = 64;     // samples between twiddles taken from the table
 
 __global__ __launch_bounds__(kMelThreads) void mel_kernel(
     const float* __restrict__ tail_in, float* __restrict__ tail_out,
@@ -52,15 +53,27 @@ __global__ __launch_bounds__(kMelThreads) void mel_kernel(
       tail_out[(int64_t)s * keep + n] = xin[per_step - keep + n];
   }
   __syncthreads();
+  // Bin k's twiddles cos/sin(2 pi k n / n_fft) advance by a rotation through
+  // 2 pi k / n_fft per sample, restarted from the table every kMelResync
+  // samples (so the float32 recurrence drifts by at most that many
+  // roundings).  Reading the table at k n mod n_fft for every sample would put
+  // the lanes of a wave n entries apart in LDS: bank conflicts for most n.
   const int bins = n_fft / 2 + 1;
   for (int k = threadIdx.x; k < bins; k += kMelThreads) {
+    const float cw = scos[k], sw = ssin[k];
     float re = 0.f, im = 0.f;
-    int m = 0;                                           // k * n mod n_fft
-    for (int n = 0; n < n_fft; ++n) {
-      re = fmaf(sx[n], scos[m], re);
-      im = fmaf(sx[n], ssin[m], im);
-      m += k;
-      if (m >= n_fft) m -= n_fft;
+    for (int n0 = 0; n0 < n_fft; n0 += kMelResync) {
+      const int m0 = (int)(((int64_t)k * n0) % n_fft);
+      float tc = scos[m0], ts = ssin[m0];
+      const int n1 = min(n0 + kMelResync, n_fft);
+      for (int n = n0; n < n1; ++n) {
+        const float x = sx[n];
+        re = fmaf(x, tc, re);
+        im = fmaf(x, ts, im);
+        const float nc = fmaf(tc, cw, -ts * sw);
+        ts = fmaf(tc, sw, ts * cw);
+        tc = nc;
+      }
     }
     spow[k] = fmaf(re, re, im * im);
   }
