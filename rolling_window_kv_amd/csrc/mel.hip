@@ -8,7 +8,7 @@
 // samples: frame f of a step covers samples [f*hop, f*hop + n_fft) of
 // tail ++ new samples, so every frame is causal and a step of n samples
 // yields n / hop frames.  One workgroup per (stream, frame): the windowed
-// frame and a twiddle table sit in LDS, a thread per DFT bin sums the real
+// frame and a twiddle table sit in LDS, two threads per DFT bin sum the real
 // DFT in float32 (its twiddles by rotation, see below), and a thread per mel
 // band applies its filter row and the log.  The new tail is the last n_fft - hop new samples (the step carries
 // at least that many), written to a second buffer so that no workgroup reads
@@ -23,7 +23,8 @@
 namespace rkv {
 namespace {
 
-constexpr int kMelThreads = 256;
+constexpr int kMelThreads = 512;
+constexpr int kMelParts = 2;       // lanes per DFT bin (a power of 2 dividing 64)
 constexpr int kMelResync = 64;     // samples between twiddles taken from the table
 
 __global__ __launch_bounds__(kMelThreads) void mel_kernel(
@@ -58,14 +59,19 @@ __global__ __launch_bounds__(kMelThreads) void mel_kernel(
   // samples (so the float32 recurrence drifts by at most that many
   // roundings).  Reading the table at k n mod n_fft for every sample would put
   // the lanes of a wave n entries apart in LDS: bank conflicts for most n.
+  // kMelParts adjacent lanes share a bin, one part of the frame each, and
+  // add their sums with shuffles.
   const int bins = n_fft / 2 + 1;
-  for (int k = threadIdx.x; k < bins; k += kMelThreads) {
+  const int part = (n_fft + kMelParts - 1) / kMelParts;
+  for (int u = threadIdx.x; u < kMelParts * bins; u += kMelThreads) {
+    const int k = u / kMelParts, h = u % kMelParts;
     const float cw = scos[k], sw = ssin[k];
     float re = 0.f, im = 0.f;
-    for (int n0 = 0; n0 < n_fft; n0 += kMelResync) {
+    const int nb = h * part, ne = min(n_fft, nb + part);
+    for (int n0 = nb; n0 < ne; n0 += kMelResync) {
       const int m0 = (int)(((int64_t)k * n0) % n_fft);
       float tc = scos[m0], ts = ssin[m0];
-      const int n1 = min(n0 + kMelResync, n_fft);
+      const int n1 = min(n0 + kMelResync, ne);
       for (int n = n0; n < n1; ++n) {
         const float x = sx[n];
         re = fmaf(x, tc, re);
@@ -75,7 +81,12 @@ __global__ __launch_bounds__(kMelThreads) void mel_kernel(
         tc = nc;
       }
     }
-    spow[k] = fmaf(re, re, im * im);
+#pragma unroll
+    for (int off = 1; off < kMelParts; off <<= 1) {
+      re += __shfl_xor(re, off);
+      im += __shfl_xor(im, off);
+    }
+    if (h == 0) spow[k] = fmaf(re, re, im * im);
   }
   __syncthreads();
   float* o = out + ((int64_t)s * (per_step / hop) + f) * n_mels;
