@@ -805,12 +805,14 @@ int choose_splits(const rkv_cfg* cfg, int32_t slots) {
   // merge launch cost more than its parallelism gains (measured: one split
   // is fastest at W = 375 for any item count, six help at W = 2048 up to 32
   // items).  Re-basing every position with the residual costs several times
-  // more per key, so there splits of 64 keys still pay.
+  // more per key, so there splits of about 48 keys still pay (measured at
+  // W = 375, one item per head: 8 splits 12.8 us a step, 5 splits 14.1, 12
+  // splits 13.4).
   const int64_t items = (int64_t)cfg->num_layers * cfg->num_streams * cfg->num_kv_heads;
   const int64_t target = 2048;
   int64_t n = (target + items - 1) / items;
   const bool heavy = (cfg->flags & RKV_F_COMPENSATED) && cfg->rebase_chunk == 1;
-  const int64_t max_split = slots / (heavy ? 64 : 256);
+  const int64_t max_split = heavy ? (slots + 24) / 48 : slots / 256;
   if (n > max_split) n = max_split;
   if (n > kMaxSplits) n = kMaxSplits;
   if (n < 1) n = 1;

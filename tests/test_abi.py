@@ -134,9 +134,11 @@ def test_workspace_sizes(rkv):
     assert rkv.rkv_workspace_bytes(good_cfg(rkv, **one), 375) == 0
     # ... with 2048 keys: 8 ranges (2 items, 2048 / 256 keys each)
     assert rkv.rkv_workspace_bytes(good_cfg(rkv, **one), 2048) == 2 * 8 * (16 + 8 * 128) * 4
-    # re-base every position with the residual: splits of 64 keys, 375 // 64 = 5
+    # re-base every position with the residual: splits of about 48 keys,
+    # round(375 / 48) = 8, round(250 / 48) = 5
     comp = good_cfg(rkv, rebase_chunk=1, flags=rkv.RKV_F_COMPENSATED, **one)
-    assert rkv.rkv_workspace_bytes(comp, 375) == 2 * 5 * (16 + 8 * 128) * 4
+    assert rkv.rkv_workspace_bytes(comp, 375) == 2 * 8 * (16 + 8 * 128) * 4
+    assert rkv.rkv_workspace_bytes(comp, 250) == 2 * 5 * (16 + 8 * 128) * 4
     # an explicit count is kept up to one split per 16 slots and 64 in all
     assert rkv.rkv_workspace_bytes(good_cfg(rkv, num_splits=6, **one), 375) == \
         2 * 6 * (16 + 8 * 128) * 4
