@@ -702,6 +702,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a) {
   const int ns = a.nsplit;
   const int64_t pf = partial_floats(D);
   const float* base = a.ws + (int64_t)item * ns * pf;
+  // A thread's partials of the first 8 splits are read at once, together with
+  // the maxima and sums (they do not depend on them): one round trip to
+  // memory for up to 8 splits instead of two.
+  const int idx = threadIdx.x;
+  const bool live = idx < a.G * D;
+  const int h = live ? idx / D : 0;
+  const int d = idx - h * D;
+  const float* num_p = base + 16 + h * D + d;
+  float v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = live && u < ns ? num_p[u * pf] : 0.f;
   for (int i = threadIdx.x; i < ns * 8; i += kCombineThreads) {
     const int j = i >> 3, h = i & 7;
     sm_m[j][h] = base[j * pf + h];
@@ -709,29 +720,26 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a) {
   }
   __syncthreads();
   if ((int)threadIdx.x < a.G) {
-    const int h = threadIdx.x;
+    const int hh = threadIdx.x;
     float M = -INFINITY;
-    for (int j = 0; j < ns; ++j) M = fmaxf(M, sm_m[j][h]);
+    for (int j = 0; j < ns; ++j) M = fmaxf(M, sm_m[j][hh]);
     float den = 0.f;
     for (int j = 0; j < ns; ++j) {
-      const float mj = sm_m[j][h];
+      const float mj = sm_m[j][hh];
       const float f = (M == -INFINITY || mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
-      sm_f[j][h] = f;
-      den += f * sm_l[j][h];
+      sm_f[j][hh] = f;
+      den += f * sm_l[j][hh];
     }
-    sm_den[h] = den;
+    sm_den[hh] = den;
   }
   __syncthreads();
-  const int idx = threadIdx.x;
-  if (idx >= a.G * D) return;
-  const int h = idx / D;
-  const int d = idx - h * D;
-  const float* num_p = base + 16 + h * D + d;
+  if (!live) return;
   float num = 0.f;
   for (int j0 = 0; j0 < ns; j0 += 8) {
-    float v[8];
+    if (j0 > 0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = j0 + u < ns ? num_p[(j0 + u) * pf] : 0.f;
+      for (int u = 0; u < 8; ++u) v[u] = j0 + u < ns ? num_p[(j0 + u) * pf] : 0.f;
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (j0 + u < ns) num += sm_f[j0 + u][h] * v[u];
