@@ -93,7 +93,7 @@ def test_multi_stream_mixed_windows_chunked_rebase(outlier):
                             f"l{l} s{s} vs exact")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 5])
+@pytest.mark.parametrize("splits", [1, 2, 5, 12])     # 12: the merge reads partials in two chunks
 def test_split_key_ranges_agree(splits):
     rkv = rkv_mod()
     dev = device()
