@@ -1,7 +1,8 @@
 """The rolling log-mel front end on the GPU against the float64 oracle
-(voxtral.c explainer, section 三: the mel buffer rolls): 12 steps of 1280
-samples for 5 streams of noise, tones and silence, compared frame by frame
-with the oracle's rolling buffer; the carried tail bit-exact."""
+(voxtral.c explainer, section 三: the mel buffer rolls): 12 steps for 5
+streams of noise, tones and silence, at the 80 ms step (1280 samples, n_fft
+400, hop 160) and with an odd 401-sample frame, compared frame by frame with
+the oracle's rolling buffer; the carried tail bit-exact."""
 import numpy as np
 import pytest
 import torch
@@ -25,26 +26,31 @@ def _audio(seed, S, T):
     return x.astype(np.float32)
 
 
-def test_rolling_mel_matches_oracle():
+@pytest.mark.parametrize("n_fft,hop,n_mels,per", [
+    (400, 160, 128, 1280),      # the 80 ms step of 16 kHz audio
+    (401, 100, 80, 800),        # odd frame: the two halves of each DFT sum differ in length
+])
+def test_rolling_mel_matches_oracle(n_fft, hop, n_mels, per):
     rkv = rkv_mod()
     dev = device()
-    S, steps, per = 5, 12, 1280
-    cfg = rkv.make_mel_cfg(S)
+    S, steps = 5, 12
+    say(f"mel: n_fft={n_fft} hop={hop} n_mels={n_mels} samples/step={per}")
+    cfg = rkv.make_mel_cfg(S, n_fft=n_fft, hop=hop, n_mels=n_mels, samples_per_step=per)
     fe = rkv.MelFrontend(cfg, device=dev)
     x = _audio(5, S, steps * per)
     xd = torch.from_numpy(x).to(dev)
-    out = torch.empty((steps, S, per // 160, 128), dtype=torch.float32, device=dev)
+    out = torch.empty((steps, S, per // hop, n_mels), dtype=torch.float32, device=dev)
     for i in range(steps):
         fe.step(xd[:, i * per:(i + 1) * per].contiguous(), out[i])
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     filters = fe.filters.cpu().numpy().astype(np.float64)
     for s in range(S):
-        roll = mel.RollingMel(filters=filters)       # the same float32 filterbank
+        roll = mel.RollingMel(n_fft=n_fft, hop=hop, filters=filters)  # the same float32 filterbank
         want = np.stack([roll.step(x[s, i * per:(i + 1) * per].astype(np.float64))
                          for i in range(steps)])
         eg, ew = 10.0 ** got[:, s], 10.0 ** want
-        # float32 DFT sums of 400 terms: energy error within 2e-5 of the
+        # float32 DFT sums of ~400 terms: energy error within 2e-5 of the
         # frame's largest band plus 1e-4 of the band itself
         tol = 2e-5 * ew.max(axis=-1, keepdims=True) + 1e-4 * ew
         err = np.abs(eg - ew)
@@ -53,5 +59,5 @@ def test_rolling_mel_matches_oracle():
             f"{float(np.abs(got[:, s] - want)[ew > 1e-6 * ew.max(-1, keepdims=True)].max()):.2e}")
         assert np.all(err <= tol)
         tail = fe.tails[fe.parity][s].cpu().numpy()
-        np.testing.assert_array_equal(tail, x[s, steps * per - 240:steps * per])
+        np.testing.assert_array_equal(tail, x[s, steps * per - (n_fft - hop):steps * per])
     assert np.all(got[:, 2] == np.float32(np.log10(np.float32(1e-10))))   # silence
