@@ -261,10 +261,11 @@ def run_gpu(c, args):
         # layer l's output would make them; the step plan is shared
         if c["mode"] == "enc":
             cfg1 = rkv.make_cfg(S, 1, num_q_heads=c["H"], num_kv_heads=c["H"], head_dim=c["d"],
-                                mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=c["F"])
+                                mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=c["F"],
+                                max_cap=cfg.max_cap)
         else:
             cfg1 = rkv.make_cfg(S, 1, mode=cfg.mode, rebase_chunk=cfg.rebase_chunk,
-                                flags=cfg.flags, num_splits=args.splits)
+                                flags=cfg.flags, num_splits=args.splits, max_cap=cfg.max_cap)
         views = [rkv.kv_view(cache.k[l:l + 1], cache.v[l:l + 1],
                              None if cache.k_lo is None else cache.k_lo[l:l + 1])
                  for l in range(L)]

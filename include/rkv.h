@@ -37,9 +37,18 @@
  *   - Element type of K, V, q, k_new, v_new is bfloat16 (raw 16-bit patterns).
  *     Output is bfloat16, or float32 with RKV_F_OUT_F32.
  *   - Rotary embedding: theta_i = rope_base^(-2i/d), i < d/2; element i pairs
- *     with element i + d/2 (half-split).  Angles, their cosines/sines and every
- *     rotation of a stored K are float64, and the stored bfloat16 is the
- *     correctly rounded (nearest, ties to even) value of the float64 result.
+ *     with element i + d/2 (half-split).  Angles and their cosines/sines are
+ *     float64.  An appended K (rkv_append and the appends inside the fused
+ *     calls) is rotated in float64 and stored as the correctly rounded
+ *     (nearest, ties to even) value.  A re-base of stored K (rkv_roll_rebase
+ *     and the re-bases inside the fused calls) is rotated in float32
+ *     double-float arithmetic (cos/sin split into float32 hi + lo, product
+ *     errors recovered with FMAs) and rounded to nearest: within 1 ulp of the
+ *     correctly rounded float64 rotation.
+ *   - Capacity: rkv_cfg.max_cap declares the rows per (layer, stream, head)
+ *     the caller's rings hold.  rkv_state_init rejects a stream capacity above
+ *     it and every call that takes an rkv_kv_view rejects kv->slots below it
+ *     (RKV_ESTATE), so no stream state can address a row the ring lacks.
  */
 #ifndef RKV_H
 #define RKV_H
@@ -61,7 +70,8 @@ typedef enum rkv_status {
   RKV_EINVAL = -1,       /* null pointer, non-positive size, inconsistent sizes */
   RKV_EUNSUPPORTED = -2, /* head_dim not 64/128, group > 8, F > 8, unknown mode/flag */
   RKV_EALIGN = -3,       /* pointer not 16-byte aligned or stride not a multiple of 8 elements */
-  RKV_ESTATE = -4,       /* per-stream window/capacity/origin inconsistent with the mode */
+  RKV_ESTATE = -4,       /* per-stream window/capacity/origin inconsistent with the mode,
+                            or a ring with fewer slots than cfg->max_cap */
   RKV_EHIP = -5,         /* a HIP launch failed; see rkv_last_hip_error() */
   RKV_ESPACE = -6        /* workspace smaller than rkv_workspace_bytes() */
 } rkv_status;
@@ -103,7 +113,10 @@ typedef struct rkv_cfg {
                             per 16 slots are used; 0 = library choice */
   double rope_base;      /* > 0, e.g. 1e6 */
   float softmax_scale;   /* 0 = 1/sqrt(d) */
-  int32_t reserved;
+  int32_t max_cap;       /* rows per (layer, stream, head) of the rings: >= every stream's
+                            capacity and <= kv->slots (RKV_ESTATE otherwise); >= 1 for
+                            rkv_state_init* and every call taking an rkv_kv_view
+                            (RKV_EINVAL otherwise), unused by the others */
 } rkv_cfg;
 
 /* Per-stream cache state (device memory, S entries, 48 bytes each).
@@ -175,7 +188,8 @@ int rkv_validate_cfg(const rkv_cfg* cfg);
 /* Fill h_state[0..S) (host memory) for streams starting at h_origin[s] with
  * window h_window[s] and capacity h_cap[s].  Required: REBASE cap == window;
  * COMPACT cap > window (the voxtral.c window plus room to grow before the next
- * compaction); ENC_CHUNK cap >= window + new_rows; origin >= 0.  The caller
+ * compaction); ENC_CHUNK cap >= window + new_rows; cap <= cfg->max_cap;
+ * origin >= 0 (RKV_ESTATE otherwise; RKV_EINVAL for max_cap < 1).  The caller
  * copies the array to device memory (S * sizeof(rkv_stream_state) bytes). */
 int rkv_state_init_host(const rkv_cfg* cfg, const int32_t* h_window,
                         const int32_t* h_cap, const int64_t* h_origin,

@@ -62,7 +62,10 @@ int check_kv(const rkv_cfg* c, const rkv_kv_view* kv) {
   if (!kv || !kv->k || !kv->v) return RKV_EINVAL;
   const bool comp = (c->flags & RKV_F_COMPENSATED) != 0;
   if (comp && !kv->k_lo) return RKV_EINVAL;
-  if (kv->slots < 1) return RKV_EINVAL;
+  if (kv->slots < 1 || c->max_cap < 1) return RKV_EINVAL;
+  // every stream's capacity is at most max_cap (checked when the states were
+  // built), so a ring of at least max_cap slots holds every row a plan names
+  if (kv->slots < c->max_cap) return RKV_ESTATE;
   if (kv->slot_stride < c->head_dim || kv->layer_stride < 0 || kv->stream_stride < 0 ||
       kv->head_stride < 0)
     return RKV_EINVAL;
@@ -180,10 +183,11 @@ int rkv_state_init_host(const rkv_cfg* cfg, const int32_t* h_window, const int32
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (!h_window || !h_cap || !h_origin || !h_state) return RKV_EINVAL;
+  if (cfg->max_cap < 1) return RKV_EINVAL;
   for (int s = 0; s < cfg->num_streams; ++s) {
     const int32_t W = h_window[s], cap = h_cap[s];
     const int64_t origin = h_origin[s];
-    if (W < 1 || cap < 1 || origin < 0) return RKV_ESTATE;
+    if (W < 1 || cap < 1 || origin < 0 || cap > cfg->max_cap) return RKV_ESTATE;
     switch (cfg->mode) {
       case RKV_MODE_REBASE:
         if (cap != W) return RKV_ESTATE;

@@ -192,6 +192,8 @@ void attn_kernel(AttnArgs a) {
   const int slots = a.ring.slots;
   const int per = (((slots + a.nsplit - 1) / a.nsplit) + TK - 1) & ~(TK - 1);
   const int kb = split * per;
+  // n_valid <= cap <= slots is guaranteed by the host checks; the clamp only
+  // bounds the reads of a corrupted plan
   const int n_valid = P->n_valid < slots ? P->n_valid : slots;
   const int ke = kb + per < n_valid ? kb + per : n_valid;
 

@@ -33,7 +33,9 @@ __device__ __forceinline__ void append_unit(const rkv_step_plan* __restrict__ pl
   const rkv_step_plan* P = plan + s;
   if (j >= P->new_rows) return;
   const int slot = (P->slot + j) % P->cap;
-  if (slot >= ring.slots) return;  // state capacity beyond the allocated rows
+  // The host rejects rings with fewer slots than any stream's capacity; this
+  // only keeps a corrupted plan from writing outside the ring.
+  if (slot >= ring.slots) return;
   const int64_t in_off =
       ENC ? ((((int64_t)l * S + s) * F + j) * H + g) * D : (((int64_t)l * S + s) * H + g) * D;
   const int64_t row = (int64_t)l * ring.ls + (int64_t)s * ring.ss + (int64_t)g * ring.hs +
@@ -291,6 +293,7 @@ __global__ __launch_bounds__(256) void compact_kernel(const rkv_step_plan* __res
   item_coords(blockIdx.x, H, S, l, s, g);
   const rkv_step_plan* P = plan + s;
   const int drop = P->compact_drop;
+  // (cap > slots cannot pass the host checks; kept as a bound on a corrupted plan)
   if (drop == 0 || P->cap > ring.slots) return;
   const int rows = P->window;
   uint16_t* base = (blockIdx.y == 0 ? ring.k : ring.v) + (int64_t)l * ring.ls +

@@ -74,7 +74,7 @@ class rkv_cfg(ctypes.Structure):
         ("rebase_chunk", ctypes.c_int32), ("new_rows", ctypes.c_int32),
         ("flags", ctypes.c_uint32), ("num_splits", ctypes.c_int32),
         ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-        ("reserved", ctypes.c_int32),
+        ("max_cap", ctypes.c_int32),
     ]
 
 
@@ -201,9 +201,12 @@ def lib_path():
 
 def make_cfg(num_streams, num_layers, num_q_heads=16, num_kv_heads=2, head_dim=128,
              mode=RKV_MODE_REBASE, rebase_chunk=1, new_rows=1, flags=0, num_splits=0,
-             rope_base=1e6, softmax_scale=0.0) -> rkv_cfg:
+             rope_base=1e6, softmax_scale=0.0, max_cap=0) -> rkv_cfg:
+    """max_cap: ring rows per (layer, stream, head); 0 leaves it to :class:`Cache`,
+    which declares its own slot count."""
     return rkv_cfg(num_streams, num_layers, num_q_heads, num_kv_heads, head_dim, mode,
-                   rebase_chunk, new_rows, flags, num_splits, rope_base, softmax_scale, 0)
+                   rebase_chunk, new_rows, flags, num_splits, rope_base, softmax_scale,
+                   max_cap)
 
 
 def _ptr(t):
@@ -523,6 +526,8 @@ class Cache:
     def __init__(self, cfg, slots, window, cap, origin=0, device="cuda", zero=True,
                  layout="interleaved"):
         import torch
+        if cfg.max_cap == 0:
+            cfg.max_cap = slots      # the rings below hold `slots` rows per head
         self.cfg = cfg
         L, S, H, d = cfg.num_layers, cfg.num_streams, cfg.num_kv_heads, cfg.head_dim
         comp = bool(cfg.flags & RKV_F_COMPENSATED)

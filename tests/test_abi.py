@@ -63,7 +63,7 @@ def test_version_and_strerror(rkv):
 
 def good_cfg(rkv, **kw):
     base = dict(num_streams=4, num_layers=2, num_q_heads=16, num_kv_heads=2, head_dim=128,
-                mode=rkv.RKV_MODE_REBASE, rebase_chunk=25)
+                mode=rkv.RKV_MODE_REBASE, rebase_chunk=25, max_cap=375)
     base.update(kw)
     return rkv.make_cfg(**base)
 
@@ -100,7 +100,7 @@ def test_state_init_matches_oracle(rkv, mode, W, cap, dc, F):
     kw = dict(mode=mode, rebase_chunk=dc, new_rows=F)
     if mode == 2:
         kw.update(num_q_heads=20, num_kv_heads=20, head_dim=64)
-    cfg = good_cfg(rkv, **kw)
+    cfg = good_cfg(rkv, max_cap=cap, **kw)
     origins = np.array([0, 1, 4321, 5000], np.int64)
     st = rkv.rkv_state_init_host(cfg, W, cap, origins)
     for s in range(4):
@@ -117,13 +117,63 @@ def test_state_init_rejects_inconsistent_streams(rkv):
     assert e.value.status == rkv.RKV_ESTATE
     with pytest.raises(rkv.RkvError):
         rkv.rkv_state_init_host(cfg, 375, 375, -1)
-    ccfg = good_cfg(rkv, mode=rkv.RKV_MODE_COMPACT)
+    ccfg = good_cfg(rkv, mode=rkv.RKV_MODE_COMPACT, max_cap=9216)
     with pytest.raises(rkv.RkvError):
         rkv.rkv_state_init_host(ccfg, 8192, 8192, 0)
     ecfg = good_cfg(rkv, mode=rkv.RKV_MODE_ENC_CHUNK, num_q_heads=20, num_kv_heads=20,
-                    head_dim=64, new_rows=4)
+                    head_dim=64, new_rows=4, max_cap=754)
     with pytest.raises(rkv.RkvError):
         rkv.rkv_state_init_host(ecfg, 750, 753, 0)
+
+
+def test_capacity_beyond_the_ring_is_rejected(rkv):
+    """A stream capacity above cfg.max_cap fails at state set-up, and a ring
+    with fewer slots than cfg.max_cap fails every call that takes it, so no
+    state can name a row the ring lacks (voxtral.c explainer, section 二: the
+    buffer's capacity kv_cache_max bounds every row index)."""
+    ccfg = good_cfg(rkv, mode=rkv.RKV_MODE_COMPACT, max_cap=9000)
+    with pytest.raises(rkv.RkvError) as e:
+        rkv.rkv_state_init_host(ccfg, 8192, 9216, 0)          # cap 9216 > max_cap 9000
+    assert e.value.status == rkv.RKV_ESTATE
+    assert rkv.rkv_state_init_host(ccfg, 8192, 9000, 0)["cap"][0] == 9000
+    ecfg = good_cfg(rkv, mode=rkv.RKV_MODE_ENC_CHUNK, num_q_heads=20, num_kv_heads=20,
+                    head_dim=64, new_rows=4, max_cap=753)
+    with pytest.raises(rkv.RkvError) as e:
+        rkv.rkv_state_init_host(ecfg, 750, 754, 0)
+    assert e.value.status == rkv.RKV_ESTATE
+    unset = good_cfg(rkv, max_cap=0)
+    with pytest.raises(rkv.RkvError) as e:
+        rkv.rkv_state_init_host(unset, 375, 375, 0)
+    assert e.value.status == rkv.RKV_EINVAL
+    W = np.full(unset.num_streams, 375, np.int32)
+    O = np.zeros(unset.num_streams, np.int64)
+    assert call(rkv, "rkv_state_init", ctypes.byref(unset), ctypes.c_void_p(FAKE), W.ctypes.data,
+                W.ctypes.data, O.ctypes.data, None) == rkv.RKV_EINVAL
+    # a 374-slot ring for states of capacity up to 375
+    cfg = good_cfg(rkv)
+    short = fake_view(rkv, slots=374)
+    F, N = ctypes.c_void_p(FAKE), None
+    c, k = ctypes.byref(cfg), ctypes.byref(short)
+    assert call(rkv, "rkv_append", c, F, k, F, F, N) == rkv.RKV_ESTATE
+    assert call(rkv, "rkv_update_step", c, F, k, F, F, N) == rkv.RKV_ESTATE
+    assert call(rkv, "rkv_roll_rebase", c, F, k, N) == rkv.RKV_ESTATE
+    assert call(rkv, "rkv_decode_attn", c, F, k, F, F, N, 0, N) == rkv.RKV_ESTATE
+    assert call(rkv, "rkv_decode_step", c, F, k, F, F, F, F, N, 0, N) == rkv.RKV_ESTATE
+    PL = ctypes.c_void_p(FAKE + 0x100000)
+    assert call(rkv, "rkv_decode_step_pipelined", c, F, F, PL, k, F, F, F, F, N, 0,
+                N) == rkv.RKV_ESTATE
+    assert call(rkv, "rkv_decode_attn_pipelined", c, F, F, PL, k, F, F, N, 0,
+                N) == rkv.RKV_ESTATE
+    comp = good_cfg(rkv, mode=rkv.RKV_MODE_COMPACT)
+    assert call(rkv, "rkv_compact", ctypes.byref(comp), F, k, N) == rkv.RKV_ESTATE
+    enc = good_cfg(rkv, mode=rkv.RKV_MODE_ENC_CHUNK, num_q_heads=20, num_kv_heads=20,
+                   head_dim=64, new_rows=4)
+    assert call(rkv, "rkv_encoder_chunk_attn", ctypes.byref(enc), F, k, F, F, F, F, N, 0,
+                N) == rkv.RKV_ESTATE
+    # the same ring with max_cap unset: rejected as an invalid configuration
+    assert call(rkv, "rkv_append", ctypes.byref(unset), F, ctypes.byref(fake_view(rkv)), F, F,
+                N) == rkv.RKV_EINVAL
+    assert rkv.rkv_last_hip_error() == 0
 
 
 def test_workspace_sizes(rkv):
@@ -287,7 +337,7 @@ def test_encoder_step_sizes_and_validation(rkv):
     S, L, H, d, F, slots, ffn = 2, 3, 4, 64, 4, 24, 1024
     hidden = H * d
     cfg = rkv.make_cfg(S, L, num_q_heads=H, num_kv_heads=H, head_dim=d,
-                       mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F)
+                       mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F, max_cap=slots)
     ec = rkv.make_encoder_cfg(ffn=ffn, norm_eps=1e-5)
     # g1, wq, wk, wv, wo, g2, w1, w2 in bfloat16
     assert rkv.rkv_encoder_layer_weight_bytes(cfg, ec) == 2 * (2 * hidden + 4 * hidden ** 2
@@ -320,7 +370,8 @@ def test_encoder_step_sizes_and_validation(rkv):
     assert step(c, e, P, k, ctypes.c_void_p(FAKE + 0x3000004), X, WS, ws, N) == rkv.RKV_EALIGN
     assert step(c, e, P, k, W, X, WS, ws - 1, N) == rkv.RKV_ESPACE
     f32 = rkv.make_cfg(S, L, num_q_heads=H, num_kv_heads=H, head_dim=d,
-                       mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F, flags=rkv.RKV_F_OUT_F32)
+                       mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=F, flags=rkv.RKV_F_OUT_F32,
+                       max_cap=slots)
     assert step(ctypes.byref(f32), e, P, k, W, X, WS, ws, N) == rkv.RKV_EUNSUPPORTED
     assert step(ctypes.byref(dec), e, P, k, W, X, WS, ws, N) == rkv.RKV_EINVAL
     assert step(c, ctypes.byref(bad[0]), P, k, W, X, WS, ws, N) == rkv.RKV_EINVAL

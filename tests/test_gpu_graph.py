@@ -18,7 +18,8 @@ def test_per_layer_step_graph_replays_match_eager_calls():
     dev = device()
     L, S, W, dc, P, steps = 3, 4, 40, 5, 3, 60
     cfg = rkv.make_cfg(S, L, rebase_chunk=dc)
-    cfg1 = rkv.make_cfg(S, 1, rebase_chunk=dc, num_splits=3)     # split + merge launches
+    cfg1 = rkv.make_cfg(S, 1, rebase_chunk=dc, num_splits=3,      # split + merge launches
+                        max_cap=W)
     origins = np.array([0, 2, 9, 31], np.int64)
     gen = torch.Generator().manual_seed(31)
     q = torch.randn((P, L, S, 16, 128), generator=gen).to(torch.bfloat16).to(dev)

@@ -19,6 +19,7 @@ FIELDS = ("t", "pos", "pos_offset", "first_pos", "evict_pos", "slot", "n_valid",
 def _run(rkv, cfg, windows, caps, origins, steps, dc, F):
     dev = device()
     S = cfg.num_streams
+    cfg.max_cap = int(np.max(caps))
     host = rkv.rkv_state_init_host(cfg, windows, caps, origins)
     state = torch.from_numpy(host.view(np.uint8).copy()).to(dev)
     plan = torch.zeros(S * rkv.PLAN_DTYPE.itemsize, dtype=torch.uint8, device=dev)
@@ -87,7 +88,7 @@ def test_device_state_init_equals_host_build():
     dev = device()
     S = 300
     say(f"state init: S={S}")
-    cfg = rkv.make_cfg(S, 2, rebase_chunk=25)
+    cfg = rkv.make_cfg(S, 2, rebase_chunk=25, max_cap=375)
     rng = np.random.default_rng(7)
     windows = rng.choice(np.array([375, 250, 188], np.int32), S)
     origins = rng.integers(0, 5000, S).astype(np.int64)
