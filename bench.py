@@ -90,6 +90,54 @@ def bytes_per_sl_step(c):
     return W * 2 * row + 2 * F * row + 2 * F * row + 2 * F * row  # cached read, q/out, new in, append
 
 
+def launch_bytes(c, windows, origins, steps):
+    """Algorithmic bytes of the attention launches (with the cache updates of
+    the step) at the given step numbers (0 = a stream's first step), summed
+    over the launches, every layer and stream: the attended K+V rows, q and
+    out, the new K/V rows read and appended, and on a re-base step the rotated
+    K of the retained rows written (plus, compensated, their residuals read
+    and written).  The compaction move runs in its own launch and is not
+    charged here."""
+    L, S = c["L"], c["S"]
+    windows = np.asarray(windows, np.int64)
+    origins = np.asarray(origins, np.int64)
+    total = 0.0
+    if c["mode"] == "enc":
+        return float(bytes_per_sl_step(c)) * L * S * len(steps)
+    Hq, Hkv, d = 16, 2, 128
+    row = Hkv * d * 2
+    fixed = 2 * Hq * d * 2 + 2 * row + 2 * row          # q, out; new K/V in; appended K/V
+    if c["mode"] == "compact":
+        W, cap = c["W"], c["cap"]
+        need = max(steps) + 1
+        rows = np.empty(need, np.int64)                  # rows attended at each step
+        n = 0
+        for t in range(need):
+            if n >= cap and n >= W:
+                n = W
+            n += 1
+            rows[t] = n
+        for t in steps:
+            total += S * (rows[t] * 2 * row + fixed)
+        return total * L
+    dc = c["dc"]
+    for t in steps:
+        length = np.minimum(t + 1, windows)
+        oldest = origins + t - length + 1
+        base = dc * (oldest // dc)
+        if t == 0:
+            prev = dc * (origins // dc)
+        else:
+            plen = np.minimum(t, windows)
+            prev = dc * ((origins + t - 1 - plen + 1) // dc)
+        moved = base != prev
+        b = length * 2 * row + fixed + moved * (length - 1) * row
+        if c.get("comp"):
+            b = b + moved * 2 * (length - 1) * row + row
+        total += float(b.sum())
+    return total * L
+
+
 def kernel_source_digest():
     h = hashlib.sha256()
     for name in ("attn.hip", "rkv_device.h", "rkv_internal.h"):
@@ -168,7 +216,14 @@ def cpu_baseline(c, seed, budget_s=15.0):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    workers = max(1, min(16, cores, c["S"]))
+    # one single-threaded process per core, up to one per stream and up to
+    # the job's CPU share (OMP_NUM_THREADS where the machine sets it)
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    share = share if share > 0 else cores
+    workers = max(1, min(share, cores, c["S"]))
     W = c["W"][0] if isinstance(c["W"], tuple) else c["W"]
     if c["mode"] == "compact":
         fill = (W + c["cap"]) // 2   # mid-way between two compactions
@@ -186,11 +241,23 @@ def cpu_baseline(c, seed, budget_s=15.0):
     total = sum(r[0] for r in res)
     timed = max(r[1] for r in res)
     return {"value": total / timed, "unit": "stream-layer steps/s", "cores": workers,
-            "kind": "oracle",
+            "kind": "oracle", "processes": workers, "threads_per_process": 1,
+            "host_cores": cores, "cpu_share": share, "cpu_model": cpu_model(),
             "sample": f"storage-faithful float64 oracle, 1 layer x {workers} streams, "
                       f"window pre-filled ({fill} steps untimed), then timed steps for "
-                      f"{budget_s:g} s per stream ({total} steps in all), one process per "
-                      f"stream ({wall:.1f} s wall incl. fill)"}
+                      f"{budget_s:g} s per stream ({total} steps in all), one single-threaded "
+                      f"process per stream on {workers} of the {cores} host cores "
+                      f"(CPU share {share}) ({wall:.1f} s wall incl. fill)"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -239,12 +306,14 @@ def run_gpu(c, args):
                            num_splits=args.splits)
         cache = rkv.Cache(cfg, c["cap"], c["W"], c["cap"], 0, device=dev, zero=False, layout=args.layout)
         prefill = c["cap"]
+        windows, origins = np.full(S, c["W"], np.int32), np.zeros(S, np.int64)
     else:
         cfg = rkv.make_cfg(S, L, num_q_heads=c["H"], num_kv_heads=c["H"], head_dim=c["d"],
                            mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=c["F"])
         cap = c["W"] + c["F"]
         cache = rkv.Cache(cfg, cap, c["W"], cap, 0, device=dev, zero=False, layout=args.layout)
         prefill = (cap + c["F"] - 1) // c["F"]
+        windows, origins = np.full(S, c["W"], np.int32), np.zeros(S, np.int64)
     out = torch.empty(q.shape[1:], dtype=torch.bfloat16, device=dev)
     P = q.shape[0]
     stream = torch.cuda.current_stream()
@@ -391,52 +460,60 @@ def run_gpu(c, args):
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
-    # Live kernel timing inside the timed region, sampled so that the event
-    # records barely touch the step rate (a pair around every launch costs
-    # several microseconds per step).  Pipelined decoder steps are one launch
-    # of the attention kernel each: a pair brackets RUN consecutive launches
-    # (every GAP-th run) and the mean launch duration is its time / RUN.
-    # Otherwise other kernels run between attention launches: a pair around
-    # the attention launch of every RUN-th step.
+    # Live kernel timing inside the timed region.  Pipelined decoder steps are
+    # one launch of the attention kernel each: event pairs bracket runs of RUN
+    # consecutive launches covering every timed launch (a pair around every
+    # launch costs several microseconds per step), and the mean launch
+    # duration is their total time / K.  Otherwise other kernels run between
+    # attention launches: a pair around the attention launch(es) of every
+    # RUN-th step.  Each timed launch is charged its own algorithmic bytes
+    # (launch_bytes: a re-base launch also writes the rotated K, a compaction
+    # buffer's row count varies), so the fraction follows from the launches
+    # actually timed.
     K = args.steps
-    RUN, GAP = 8, 4
-    bracket = (pipelined and args.path == "pipelined" and c["mode"] == "rebase" and K >= RUN
+    RUN = 8
+    bracket = (pipelined and args.path == "pipelined" and c["mode"] == "rebase"
                and tcond is None)
     if per_layer is not None:
         args.kernel_events = False    # the roofline uses the whole step's time
-    ev_runs, ev_steps = {}, {}
+    runs = []                          # (first, last + 1) timed-step ranges
     if args.kernel_events:
-        for n in (range(0, K - RUN + 1, RUN * GAP) if bracket else range(0, K, RUN)):
-            pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            (ev_runs if bracket else ev_steps)[n] = pair
+        runs = ([(n, min(n + RUN, K)) for n in range(0, K, RUN)] if bracket
+                else [(n, n + 1) for n in range(0, K, RUN)])
+    ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for n, _ in runs}
+    ends = {m - 1: n for n, m in runs}
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    i0 = i
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for n in range(K):
-        if n in ev_runs:
-            ev_runs[n][0].record(stream)
-        step(i, ev_steps.get(n))
-        if n - RUN + 1 in ev_runs:
-            ev_runs[n - RUN + 1][1].record(stream)
+        if bracket and n in ev:
+            ev[n][0].record(stream)
+        step(i, None if bracket else ev.get(n))
+        if bracket and n in ends:
+            ev[ends[n]][1].record(stream)
         i += 1
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     elapsed_ms = start.elapsed_time(end)
-    kernel_ms, kernel_samples = None, 0
-    if ev_runs:
-        kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_runs.values()])) / RUN
-        kernel_samples = RUN * len(ev_runs)
-    elif ev_steps:
-        kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_steps.values()]))
-        kernel_samples = len(ev_steps)
+    kernel_ms = kernel_bytes = None
+    kernel_samples = 0
+    if runs:
+        timed = [i0 + t for n, m in runs for t in range(n, m)]
+        kernel_samples = len(timed)
+        kernel_ms = sum(ev[n][0].elapsed_time(ev[n][1]) for n, _ in runs) / kernel_samples
+        kernel_bytes = launch_bytes(c, windows, origins, timed) / kernel_samples
     copy_gbps = device_copy_gbps()     # after the timed region
-    return dict(cfg=cfg, elapsed_ms=elapsed_ms, kernel_ms=kernel_ms, wall_s=wall,
-                kernel_samples=kernel_samples, copy_gbps=copy_gbps,
-                kernel_timing="event pair per run of %d back-to-back launches" % RUN
-                if ev_runs else "event pair around sampled launches",
+    return dict(cfg=cfg, elapsed_ms=elapsed_ms, kernel_ms=kernel_ms, kernel_bytes=kernel_bytes,
+                wall_s=wall, kernel_samples=kernel_samples, copy_gbps=copy_gbps,
+                first_timed_step=i0, windows=windows, origins=origins,
+                kernel_timing=("event pairs around runs of %d back-to-back launches, every "
+                               "timed launch" % RUN) if bracket
+                else "event pair around the attention launch(es) of every %d-th step" % RUN,
                 setup_s=setup_s, prefill=prefill)
 
 
@@ -629,12 +706,112 @@ def summarize_rocprof(root, last=0):
     return "\n".join(lines)
 
 
+def bench_config(args):
+    """One decoder or encoder-chunk workload (args.config) on the GPU -> (its
+    CONFIGS entry, the result line without cpu_baseline)."""
+    c = dict(CONFIGS[args.config])
+    if args.graph and not args.per_layer:
+        print("--graph applies to --per-layer", file=sys.stderr)
+        sys.exit(2)
+    if args.per_layer and (args.tcond or args.path not in (None, "fused")):
+        print("--per-layer runs rkv_advance + one fused step per layer", file=sys.stderr)
+        sys.exit(2)
+    if args.tcond and c["mode"] == "enc":
+        print("--tcond: delay conditioning applies to the decoder workloads", file=sys.stderr)
+        sys.exit(2)
+    if args.kv_fp16 and c["mode"] == "enc":
+        print("--kv-fp16: the encoder cache is bfloat16 only", file=sys.stderr)
+        sys.exit(2)
+    if args.path is None:
+        args.path = "fused" if args.per_layer else c.get("path", "pipelined")
+    args.steps = c["steps"] if args.steps is None else args.steps
+    args.warmup = c["warmup"] if args.warmup is None else args.warmup
+
+    r = run_gpu(c, args)
+    L, S, K = c["L"], c["S"], args.steps
+    secs = r["elapsed_ms"] / 1e3
+    sl_steps = L * S * K / secs
+    b_sl = bytes_per_sl_step(c)
+    step_gbps = b_sl * L * S * K / secs / 1e9
+    kernel = {"rebase": "attn_kernel<128,4,decode_fused>",
+              "compact": "attn_kernel<128,4,decode_fused>",
+              "enc": "attn_kernel<64,2,encoder_fused>"}[c["mode"]]
+    if args.path == "separate" and c["mode"] != "enc":
+        kernel = "rebase+append+attn_kernel<128,4,decode_read>"
+    if args.path == "update" and c["mode"] != "enc":
+        kernel = "update+attn_kernel<128,4,decode_read>"
+    if args.kv_fp16:
+        kernel = kernel.replace(">", ",fp16>")
+    roofline = None
+    if r["kernel_ms"]:
+        per_launch = r["kernel_bytes"]
+        achieved = per_launch / (r["kernel_ms"] / 1e3) / 1e9
+        # the stored counter figures were taken with the interleaved layout
+        traffic = (load_traffic(kernel, f"config{args.config}")
+                   if args.layout == "interleaved" else None)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                    "traffic": traffic, "kernel": kernel,
+                    "kernel_ms": round(r["kernel_ms"], 5),
+                    "kernel_launches_timed": r["kernel_samples"],
+                    "kernel_timing": r["kernel_timing"],
+                    "first_timed_step": r["first_timed_step"],
+                    "alg_bytes_per_launch": round(per_launch, 1)}
+    if args.per_layer:
+        # L launches per step: the roofline takes the whole step's time and the
+        # bytes of the timed steps
+        i0 = r["first_timed_step"]
+        per_step = launch_bytes(c, r["windows"], r["origins"], list(range(i0, i0 + K))) / K
+        gbps = per_step / (r["elapsed_ms"] / K / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                    "traffic": None,
+                    "kernel": f"{L} per-layer launches per step ({kernel})",
+                    "kernel_ms": round(r["elapsed_ms"] / K, 5),
+                    "kernel_timing": "whole step (HIP events around the timed steps)",
+                    "first_timed_step": i0,
+                    "alg_bytes_per_step": round(per_step, 1)}
+    res = {
+        "metric": METRIC,
+        "value": round(sl_steps, 1),
+        "unit": "stream-layer steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["elapsed_ms"] / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 cache, bf16 i/o" if args.kv_fp16 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": c["name"], "layers": L, "streams": S,
+                   "path": ("per-layer" + (" graph" if args.graph else "")) if args.per_layer
+                           else (args.path if c["mode"] != "enc" else "fused"),
+                   "alg_bytes_per_stream_layer_step": b_sl,
+                   **({"layout": args.layout} if args.layout != "interleaved" else {}),
+                   **({"tcond": "rkv_tcond_modulate after each step, 8 settings, dim 256"}
+                      if args.tcond else {})},
+        "achieved_GBps_step": round(step_gbps, 1),
+        "device_copy_GBps": round(r["copy_gbps"], 1),
+        "frac_of_device_copy": round(step_gbps / r["copy_gbps"], 4),
+        "hbm_frac_step": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "clock_steps_per_s": round(K / secs, 1),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    return c, res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS))
+    ap.add_argument("--config", type=int, default=None, choices=sorted(CONFIGS),
+                    help="workload (default 2, with short runs of the others reported as "
+                         "'secondary' fields of the same line)")
+    ap.add_argument("--no-secondary", dest="secondary", action="store_false",
+                    help="default run: skip the short runs of the other workloads")
     ap.add_argument("--path", choices=("pipelined", "fused", "separate", "update"),
                     default=None,
                     help="default: update for workload 3, pipelined otherwise.  "
@@ -680,6 +857,7 @@ def main():
                     help="with --summarize-rocprof: also the mean of each kernel's last N "
                          "dispatches")
     args = ap.parse_args()
+    args.path_given = args.path is not None
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof, args.summarize_last))
         return
@@ -704,94 +882,48 @@ def main():
     if args.encoder_stack:
         print(json.dumps(run_encoder_stack(args)), flush=True)
         return
-    c = dict(CONFIGS[args.config])
-    if args.graph and not args.per_layer:
-        print("--graph applies to --per-layer", file=sys.stderr)
-        sys.exit(2)
-    if args.per_layer and (args.tcond or args.path not in (None, "fused")):
-        print("--per-layer runs rkv_advance + one fused step per layer", file=sys.stderr)
-        sys.exit(2)
-    if args.tcond and c["mode"] == "enc":
-        print("--tcond: delay conditioning applies to the decoder workloads", file=sys.stderr)
-        sys.exit(2)
-    if args.kv_fp16 and c["mode"] == "enc":
-        print("--kv-fp16: the encoder cache is bfloat16 only", file=sys.stderr)
-        sys.exit(2)
-    if args.path is None:
-        args.path = "fused" if args.per_layer else c.get("path", "pipelined")
-    args.steps = c["steps"] if args.steps is None else args.steps
-    args.warmup = c["warmup"] if args.warmup is None else args.warmup
-
-    r = run_gpu(c, args)
-    L, S, K = c["L"], c["S"], args.steps
-    secs = r["elapsed_ms"] / 1e3
-    sl_steps = L * S * K / secs
-    b_sl = bytes_per_sl_step(c)
-    step_gbps = b_sl * L * S * K / secs / 1e9
-    kernel = {"rebase": "attn_kernel<128,4,decode_fused>",
-              "compact": "attn_kernel<128,4,decode_fused>",
-              "enc": "attn_kernel<64,2,encoder_fused>"}[c["mode"]]
-    if args.path == "separate" and c["mode"] != "enc":
-        kernel = "rebase+append+attn_kernel<128,4,decode_read>"
-    if args.path == "update" and c["mode"] != "enc":
-        kernel = "update+attn_kernel<128,4,decode_read>"
-    if args.kv_fp16:
-        kernel = kernel.replace(">", ",fp16>")
-    roofline = None
-    if r["kernel_ms"]:
-        per_launch = b_sl * L * S
-        achieved = per_launch / (r["kernel_ms"] / 1e3) / 1e9
-        # the stored counter figures were taken with the interleaved layout
-        traffic = (load_traffic(kernel, f"config{args.config}")
-                   if args.layout == "interleaved" else None)
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                    "traffic": traffic, "kernel": kernel,
-                    "kernel_ms": round(r["kernel_ms"], 5),
-                    "kernel_launches_timed": r["kernel_samples"],
-                    "kernel_timing": r["kernel_timing"],
-                    "alg_bytes_per_launch": per_launch}
-    if args.per_layer:
-        # L launches per step: the roofline takes the whole step's time
-        roofline = {"bound": "hbm", "achieved": round(step_gbps, 1), "peak": PEAK_HBM_GBPS,
-                    "unit": "GB/s", "frac": round(step_gbps / PEAK_HBM_GBPS, 4),
-                    "traffic": None,
-                    "kernel": f"{L} per-layer launches per step ({kernel})",
-                    "kernel_ms": round(r["elapsed_ms"] / K, 5),
-                    "kernel_timing": "whole step (HIP events around the timed steps)",
-                    "alg_bytes_per_step": b_sl * L * S}
-    res = {
-        "metric": METRIC,
-        "value": round(sl_steps, 1),
-        "unit": "stream-layer steps/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(r["elapsed_ms"] / K, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp16 cache, bf16 i/o" if args.kv_fp16 else "bf16",
-        "data": "synthetic",
-        "config": {"workload": c["name"], "layers": L, "streams": S,
-                   "path": ("per-layer" + (" graph" if args.graph else "")) if args.per_layer
-                           else (args.path if c["mode"] != "enc" else "fused"),
-                   "alg_bytes_per_stream_layer_step": b_sl,
-                   **({"layout": args.layout} if args.layout != "interleaved" else {}),
-                   **({"tcond": "rkv_tcond_modulate after each step, 8 settings, dim 256"}
-                      if args.tcond else {})},
-        "achieved_GBps_step": round(step_gbps, 1),
-        "device_copy_GBps": round(r["copy_gbps"], 1),
-        "frac_of_device_copy": round(step_gbps / r["copy_gbps"], 4),
-        "hbm_frac_step": round(step_gbps / PEAK_HBM_GBPS, 4),
-        "clock_steps_per_s": round(K / secs, 1),
-        "roofline": roofline,
-        "cpu_baseline": None,
-    }
+    explicit = args.config is not None
+    if args.config is None:
+        args.config = 2
+    c, res = bench_config(args)
     if args.cpu and not args.kv_fp16 and not args.tcond and not args.per_layer:
         res["cpu_baseline"] = cpu_baseline(c, 1000 + args.config, args.cpu_budget)
+    default_run = not (explicit or args.per_layer or args.tcond or args.kv_fp16 or args.graph
+                       or args.splits or args.layout != "interleaved" or args.path_given)
+    if default_run and args.secondary:
+        res["secondary"] = secondary_runs(args)
     print(json.dumps(res), flush=True)
 
+
+# Short runs of the other workloads, reported beside the headline line:
+# (name, overrides of the command-line arguments).
+SECONDARY = (
+    ("config1_1x1_every_step_rebase", dict(config=1)),
+    ("config2_per_layer", dict(config=2, per_layer=True, steps=200, warmup=20)),
+    ("config3_mixed_windows", dict(config=3, steps=200, warmup=20)),
+    ("config4_compaction_w8192", dict(config=4, steps=256, warmup=16)),
+    ("config5_encoder_chunks", dict(config=5, steps=100, warmup=10)),
+)
+
+
+def secondary_runs(args):
+    """Each secondary workload with its own step count; per entry the fields
+    of its own bench line that describe the measurement."""
+    import copy
+    import torch
+    out = {}
+    for name, over in SECONDARY:
+        a = copy.copy(args)
+        a.steps = a.warmup = a.path = None
+        for k, v in over.items():
+            setattr(a, k, v)
+        _, r = bench_config(a)
+        keep = ("value", "unit", "steps", "warmup", "ms_per_step", "hbm_frac_step",
+                "achieved_GBps_step", "clock_steps_per_s", "roofline")
+        out[name] = {"workload": r["config"]["workload"], "path": r["config"]["path"],
+                     **{k: r[k] for k in keep}}
+        torch.cuda.empty_cache()
+    return out
 
 if __name__ == "__main__":
     main()

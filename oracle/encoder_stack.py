@@ -22,6 +22,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
+from scipy import special
 
 from . import storage
 from .bf16 import round_bf16
@@ -33,8 +34,9 @@ def rmsnorm(x, g, eps):
 
 
 def gelu(x):
+    """Exact GELU, 0.5 x (1 + erf(x / sqrt 2)) (erf to float64 accuracy)."""
     x = np.asarray(x, np.float64)
-    return 0.5 * x * (1.0 + np.vectorize(math.erf)(x / math.sqrt(2.0)))
+    return 0.5 * x * (1.0 + special.erf(x / math.sqrt(2.0)))
 
 
 class EncoderStack:
@@ -47,6 +49,27 @@ class EncoderStack:
         self.r = rounder or (lambda x: np.asarray(x, np.float64))
         self.rings = [storage.EncoderRing(heads, d, window, frames, base, origin,
                                           rounder=rounder) for _ in weights]
+
+    def run(self, xs):
+        """xs [T, F, hidden]: T consecutive steps -> the stack's outputs [T, F, hidden].
+
+        The same values as T calls of step(), computed layer by layer: every
+        map of a layer but the chunk attention acts on each frame's row alone,
+        so a layer takes all T steps' rows at once and only its attention
+        walks the steps in order (the ring holds the earlier steps' K/V)."""
+        xs = np.asarray(xs, np.float64)
+        T = xs.shape[0]
+        r, F, H, d = self.r, self.f, self.h, self.d
+        x = xs.reshape(T * F, -1).copy()
+        for w, ring in zip(self.w, self.rings):
+            a = r(rmsnorm(x, w["g1"], self.eps))
+            q, k, v = (r(a @ w[n].T).reshape(T, F, H, d) for n in ("wq", "wk", "wv"))
+            att = np.stack([ring.step(q[t], k[t], v[t])[1] for t in range(T)])
+            x = x + r(att).reshape(T * F, H * d) @ w["wo"].T
+            a2 = r(rmsnorm(x, w["g2"], self.eps))
+            u = r(gelu(a2 @ w["w1"].T))
+            x = x + u @ w["w2"].T
+        return x.reshape(xs.shape)
 
     def step(self, x):
         """x [F, hidden] (the residual stream entering layer 0) -> after the last layer."""

@@ -174,17 +174,16 @@ class EncoderRing:
             self.k[:, slot] = hi
             self.v[:, slot] = v_new[j]
         slot_pos = sch.enc_slot_positions(plan, self.origin)
-        out = np.empty((self.f, self.h, self.d))
-        for j in range(self.f):
-            qpos = plan.pos + j
-            vis = np.array([p is not None and plan.first_pos <= p <= qpos
-                            for p in slot_pos])
-            q_rot = rope.rotate(q[j], qpos, self.base)
-            for h in range(self.h):
-                s = (self.k[h] @ q_rot[h]) * self.scale
-                s = np.where(vis, s, -np.inf)
-                s = s - s.max()
-                p = np.exp(s)
-                p /= p.sum()
-                out[j, h] = p @ self.v[h]
-        return plan, out
+        written = np.array([p is not None for p in slot_pos])
+        pos = np.array([-1 if p is None else p for p in slot_pos], np.int64)
+        # every head and frame at once: s[h, r, j] = K[h, r] . R(pos + j) q[j, h]
+        q_rot = np.stack([rope.rotate(q[j], plan.pos + j, self.base) for j in range(self.f)])
+        s = np.matmul(self.k, q_rot.transpose(1, 2, 0)) * self.scale
+        qpos = plan.pos + np.arange(self.f)
+        vis = (written & (pos >= plan.first_pos))[:, None] & (pos[:, None] <= qpos[None, :])
+        s = np.where(vis[None], s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        out = np.matmul(p.transpose(0, 2, 1), self.v).transpose(1, 0, 2)     # [F, H, d]
+        return plan, np.ascontiguousarray(out)

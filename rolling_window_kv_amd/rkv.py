@@ -413,13 +413,20 @@ class MelFrontend:
     tails (zero: every stream starts after n_fft - hop silent samples) and the
     filterbank."""
 
-    def __init__(self, cfg, sample_rate=16000.0, device="cuda"):
+    def __init__(self, cfg, sample_rate=16000.0, device="cuda", filters=None):
+        """filters: a host float32 [n_mels, n_fft // 2 + 1] filterbank to upload
+        instead of the library's (rkv_mel_filters_host)."""
         import torch
         self.cfg = cfg
         keep = cfg.n_fft - cfg.hop
         self.tails = [torch.zeros((cfg.num_streams, keep), dtype=torch.float32, device=device)
                       for _ in range(2)]
-        self.filters = torch.from_numpy(rkv_mel_filters_host(cfg, sample_rate)).to(device)
+        if filters is None:
+            filters = rkv_mel_filters_host(cfg, sample_rate)
+        filters = np.ascontiguousarray(filters, dtype=np.float32)
+        if filters.shape != (cfg.n_mels, cfg.n_fft // 2 + 1):
+            raise ValueError("filterbank must be [n_mels, n_fft // 2 + 1]")
+        self.filters = torch.from_numpy(filters).to(device)
         self.parity = 0
 
     def step(self, samples, out, stream=None):

@@ -79,3 +79,42 @@ def test_rocprof_summary_of_a_synthetic_trace(tmp_path):
     assert len(lines) == 1
     calls, mean, median, last = lines[0].split()[:4]
     assert (int(calls), float(mean), float(median), float(last)) == (3, 12.0, 12.0, 13.0)
+
+
+def test_launch_bytes_charge_each_timed_launch_its_own_work():
+    """launch_bytes (the bytes the roofline divides by) per launch: over any 25
+    consecutive full-window steps every stream re-bases exactly once, so the
+    mean equals the amortised per-step figure; a launch without a re-base and
+    a re-base launch carry their own bytes."""
+    import numpy as np
+    b = bench()
+    c = b.CONFIGS[2]
+    L, S = c["L"], c["S"]
+    win, org = np.full(S, 375, np.int32), np.zeros(S, np.int64)
+    steps = list(range(400, 425))
+    mean = b.launch_bytes(c, win, org, steps) / len(steps)
+    assert mean == pytest.approx(b.bytes_per_sl_step(c) * L * S)
+    # origin 0, W = 375, chunk 25: the base moves when the oldest retained
+    # position reaches a multiple of 25, i.e. at steps 399, 424, ...
+    plain = (375 * 1024 + 8192 + 2048) * L * S
+    assert b.launch_bytes(c, win, org, [400]) == plain
+    assert b.launch_bytes(c, win, org, [399]) == plain + 374 * 512 * L * S
+    # mixed windows and start offsets: the same identity stream by stream
+    c3 = b.CONFIGS[3]
+    S3 = c3["S"]
+    w3 = np.repeat(np.array(c3["W"], np.int32), [86, 85, 85])
+    o3 = np.random.default_rng(1).integers(0, 5000, S3).astype(np.int64)
+    m3 = b.launch_bytes(c3, w3, o3, list(range(500, 525))) / 25
+    assert m3 == pytest.approx(b.bytes_per_sl_step(c3) * c3["L"] * S3)
+    # compensated re-base every step (one stream, one layer): every launch re-bases
+    c1 = b.CONFIGS[1]
+    assert b.launch_bytes(c1, np.array([375]), np.array([0]), [700]) == \
+        pytest.approx(b.bytes_per_sl_step(c1))
+    # compaction: rows attended grow from W + 1 to the capacity between
+    # compactions; over one period the mean is the page's average length
+    c4 = b.CONFIGS[4]
+    W, cap = c4["W"], c4["cap"]
+    period = list(range(cap, cap + (cap - W)))
+    m4 = b.launch_bytes(c4, np.full(16, W), np.zeros(16, np.int64), period) / len(period)
+    want = ((W + 1 + cap) / 2 * 1024 + 8192 + 2048) * c4["L"] * c4["S"]
+    assert m4 == pytest.approx(want)

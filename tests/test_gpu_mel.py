@@ -2,7 +2,12 @@
 (voxtral.c explainer, section 三: the mel buffer rolls): 12 steps for 5
 streams of noise, tones and silence, at the 80 ms step (1280 samples, n_fft
 400, hop 160) and with an odd 401-sample frame, compared frame by frame with
-the oracle's rolling buffer; the carried tail bit-exact."""
+the oracle's rolling buffer; the carried tail bit-exact.
+
+Both sides use the oracle's filterbank (oracle.mel.mel_filters rounded to
+float32 on the host): the kernel gets it uploaded, the oracle the same
+float32 values, so no device-built value feeds the oracle.  The library's
+own filterbank (rkv_mel_filters_host) is checked against it separately."""
 import numpy as np
 import pytest
 import torch
@@ -36,7 +41,13 @@ def test_rolling_mel_matches_oracle(n_fft, hop, n_mels, per):
     S, steps = 5, 12
     say(f"mel: n_fft={n_fft} hop={hop} n_mels={n_mels} samples/step={per}")
     cfg = rkv.make_mel_cfg(S, n_fft=n_fft, hop=hop, n_mels=n_mels, samples_per_step=per)
-    fe = rkv.MelFrontend(cfg, device=dev)
+    filters32 = mel.mel_filters(sr=16000.0, n_fft=n_fft, n_mels=n_mels).astype(np.float32)
+    # the library's filterbank is the oracle's, to within a float32 rounding
+    lib_filters = rkv.rkv_mel_filters_host(cfg, 16000.0)
+    ulp = np.spacing(np.abs(filters32)).astype(np.float32)
+    assert np.all(np.abs(lib_filters - filters32) <= ulp), "rkv_mel_filters_host != oracle"
+    fe = rkv.MelFrontend(cfg, device=dev, filters=filters32)
+    assert np.array_equal(fe.filters.cpu().numpy(), filters32)
     x = _audio(5, S, steps * per)
     xd = torch.from_numpy(x).to(dev)
     out = torch.empty((steps, S, per // hop, n_mels), dtype=torch.float32, device=dev)
@@ -44,7 +55,7 @@ def test_rolling_mel_matches_oracle(n_fft, hop, n_mels, per):
         fe.step(xd[:, i * per:(i + 1) * per].contiguous(), out[i])
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
-    filters = fe.filters.cpu().numpy().astype(np.float64)
+    filters = filters32.astype(np.float64)
     for s in range(S):
         roll = mel.RollingMel(n_fft=n_fft, hop=hop, filters=filters)  # the same float32 filterbank
         want = np.stack([roll.step(x[s, i * per:(i + 1) * per].astype(np.float64))

@@ -19,6 +19,11 @@ def test_rmsnorm_and_gelu():
     want = torch.nn.functional.gelu(torch.from_numpy(y), approximate="none").numpy()
     np.testing.assert_allclose(es.gelu(y), want, rtol=1e-12, atol=1e-15)
     assert es.gelu(0.0) == 0.0
+    # the exact erf form, element by element with the standard library's erf
+    z = np.random.default_rng(3).standard_normal(2000) * 3
+    by_math = np.array([0.5 * t * (1.0 + math.erf(t / math.sqrt(2.0))) for t in z])
+    # (1 + erf) cancels for large negative arguments: an absolute bound there
+    np.testing.assert_allclose(es.gelu(z), by_math, rtol=1e-15, atol=1e-15)
 
 
 def _weights(rng, hidden, ffn):
@@ -72,3 +77,17 @@ def test_zero_output_projections_leave_the_stream_unchanged():
     st = es.EncoderStack([w, w], H, d, 6, F, 1e6, 1e-5)
     x = rng.standard_normal((F, hidden))
     np.testing.assert_array_equal(st.step(x), x)
+
+
+def test_run_over_many_steps_equals_stepping():
+    """run() (layer by layer over all steps) gives the values of step() called
+    once per step, over enough steps to wrap a ring whose size is not a
+    multiple of the chunk, with bfloat16 storage points."""
+    rng = np.random.default_rng(10)
+    H, d, F, W, hidden, ffn, T = 2, 8, 4, 10, 16, 32, 9      # ring of 14 slots
+    ws = [_weights(rng, hidden, ffn) for _ in range(2)]
+    xs = rng.standard_normal((T, F, hidden))
+    a = es.EncoderStack(ws, H, d, W, F, 1e6, 1e-5)
+    b = es.EncoderStack(ws, H, d, W, F, 1e6, 1e-5)
+    stepped = np.stack([a.step(x) for x in xs])
+    np.testing.assert_allclose(b.run(xs), stepped, rtol=1e-12, atol=1e-12)
