@@ -106,6 +106,8 @@ def _check(L, H, d, F, W, xin, wts, trace, check, end_to_end):
             want = oes.EncoderStack([wts[l]], H, d, W, F, 1e6, 1e-5).run(trace[i, :, l])
             e = float(_err(trace[i, :, l + 1], want).max())
             worst_layer = max(worst_layer, e)
+            if l % 8 == 7:
+                say(f"stream {s}: oracle layers 0..{l} done, worst {worst_layer:.3e}")
         say(f"stream {s}: worst teacher-forced layer {worst_layer:.3e} (gate {GATE:g})")
     assert worst_layer < GATE
     for i, s in enumerate(check):
@@ -113,9 +115,13 @@ def _check(L, H, d, F, W, xin, wts, trace, check, end_to_end):
             continue
         x = xin[:, s].double().numpy()
         want = oes.EncoderStack(wts, H, d, W, F, 1e6, 1e-5).run(x)
-        spread = max(float(_err(oes.EncoderStack(wts, H, d, W, F, 1e6, 1e-5,
-                                                 rounder=_perturbed_rounder(seed)).run(x),
-                                want).max()) for seed in (1, 2))
+        say(f"stream {s}: oracle stack done")
+        spread = 0.0
+        for seed in (1, 2):
+            pert = oes.EncoderStack(wts, H, d, W, F, 1e6, 1e-5,
+                                    rounder=_perturbed_rounder(seed)).run(x)
+            spread = max(spread, float(_err(pert, want).max()))
+            say(f"stream {s}: perturbed oracle run {seed} done")
         got = float(_err(trace[i, :, L], want).max())
         say(f"stream {s}: end to end max |gpu - oracle| / max(1, rms) {got:.3e}; "
             f"spread of the perturbed oracle runs {spread:.3e}; gate {2 * spread:.3e}")
