@@ -274,6 +274,24 @@ int rkv_decode_step(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
                     const void* v_new, void* out, void* workspace,
                     size_t workspace_bytes, void* hip_stream);
 
+/* rkv_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, fixed serving loops, harnesses that forbid allocation):
+ * the key-range split partials live in a device array of the library's own
+ * (RKV_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on a device
+ * until the process ends) instead of a caller workspace; no allocation, same
+ * kernels and the same results as rkv_decode_step.  The first call on a
+ * device looks the array up (hipGetSymbolAddress, not a stream operation):
+ * make one call before capturing a graph.  The current device must be the
+ * one hip_stream belongs to.  Every call on a GPU shares that GPU's array
+ * and leaves its contents behind; calls whose launches may overlap in time on
+ * one GPU (unordered streams) race and give wrong results.  Errors as
+ * rkv_decode_step, and RKV_ESPACE when rkv_workspace_bytes(cfg, kv->slots)
+ * exceeds RKV_NOALLOC_SCRATCH_BYTES (checked before any HIP call). */
+#define RKV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int rkv_decode_step_noalloc(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
+                            const rkv_kv_view* kv, const void* q, const void* k_new,
+                            const void* v_new, void* out, void* hip_stream);
+
 /* Pipelined decode step for callers that keep two plan buffers: the decode
  * step of rkv_decode_step with d_plan, and in the same launch the next step's
  * plan written to d_plan_next with d_state advanced, exactly what

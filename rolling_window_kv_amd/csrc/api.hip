@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "rkv_internal.h"
 #include "rkv_encoder.h"
 #include "rkv_mel.h"
@@ -102,6 +104,39 @@ size_t workspace_for(const rkv_cfg* c, int32_t slots) {
   return (size_t)(items * n * rkv::partial_floats(c->head_dim) * (int64_t)sizeof(float));
 }
 
+// Device array for the allocation-free entry point: each GPU the library
+// runs on holds its own copy until the process ends.  Host code never uses
+// the array's name as an address (in host code it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kScratchBytes = RKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The scratch array's device address on the current device.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return RKV_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return RKV_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RKV_OK;
+}
+
+// ws == kUseScratch: the split partials go to the library's scratch array
+// (after every argument check, so errors still come before any HIP call).
+void* const kUseScratch = reinterpret_cast<void*>(~(uintptr_t)0);
+
 int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
               const rkv_kv_view* kv, const void* q, const void* knew, const void* vnew,
               void* out, void* ws, size_t ws_bytes, void* stream,
@@ -123,7 +158,11 @@ int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
   if ((rc = check_ptr(q)) || (rc = check_ptr(out))) return rc;
   if (kind != rkv::kDecodeRead && ((rc = check_ptr(knew)) || (rc = check_ptr(vnew)))) return rc;
   const size_t need = workspace_for(cfg, kv->slots);
-  if (need) {
+  if (ws == kUseScratch) {
+    if (need > kScratchBytes) return RKV_ESPACE;
+    ws = nullptr;
+    if (need && (rc = scratch_address(&ws))) return rc;
+  } else if (need) {
     if (!ws || ws_bytes < need) return RKV_ESPACE;
     if (!aligned16(ws)) return RKV_EALIGN;
   }
@@ -395,6 +434,13 @@ int rkv_decode_step(const rkv_cfg* cfg, const rkv_step_plan* d_plan, const rkv_k
                     void* workspace, size_t workspace_bytes, void* hip_stream) {
   return attention(cfg, rkv::kDecodeFused, d_plan, kv, q, k_new, v_new, out, workspace,
                    workspace_bytes, hip_stream);
+}
+
+int rkv_decode_step_noalloc(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
+                            const rkv_kv_view* kv, const void* q, const void* k_new,
+                            const void* v_new, void* out, void* hip_stream) {
+  return attention(cfg, rkv::kDecodeFused, d_plan, kv, q, k_new, v_new, out, kUseScratch, 0,
+                   hip_stream);
 }
 
 int rkv_decode_step_pipelined(const rkv_cfg* cfg, rkv_stream_state* d_state,

@@ -33,13 +33,14 @@ RKV_F_KV_FP16 = 4
 
 RKV_MAX_NEW_ROWS = 8
 RKV_MAX_HEAD_DIM = 128
+RKV_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # Entry points declared in include/rkv.h (checked by the ABI tests).
 ENTRY_POINTS = (
     "rkv_version", "rkv_strerror", "rkv_last_hip_error", "rkv_validate_cfg",
     "rkv_state_init_host", "rkv_state_init", "rkv_workspace_bytes", "rkv_advance", "rkv_append",
     "rkv_roll_rebase", "rkv_update_step", "rkv_compact", "rkv_decode_attn", "rkv_decode_step",
-    "rkv_decode_step_pipelined", "rkv_decode_attn_pipelined",
+    "rkv_decode_step_noalloc", "rkv_decode_step_pipelined", "rkv_decode_attn_pipelined",
     "rkv_encoder_chunk_attn", "rkv_reset_streams", "rkv_restart_step",
     "rkv_mel_filters_host", "rkv_mel_step",
     "rkv_encoder_layer_weight_bytes", "rkv_encoder_step_workspace_bytes", "rkv_encoder_step",
@@ -161,6 +162,7 @@ def lib():
             "rkv_compact": ([pc, vp, pk, vp], ctypes.c_int),
             "rkv_decode_attn": ([pc, vp, pk, vp, vp, vp, sz, vp], ctypes.c_int),
             "rkv_decode_step": ([pc, vp, pk, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "rkv_decode_step_noalloc": ([pc, vp, pk, vp, vp, vp, vp, vp], ctypes.c_int),
             "rkv_decode_step_pipelined": ([pc, vp, vp, vp, pk, vp, vp, vp, vp, vp, sz, vp],
                                           ctypes.c_int),
             "rkv_decode_attn_pipelined": ([pc, vp, vp, vp, pk, vp, vp, vp, sz, vp],
@@ -484,6 +486,15 @@ def rkv_decode_step(cfg, plan, kv, q, k_new, v_new, out, workspace=None, stream=
                                                     ctypes.byref(kv), _ptr(q), _ptr(k_new),
                                                     _ptr(v_new), _ptr(out), wp, wb,
                                                     _stream(stream)))
+
+
+def rkv_decode_step_noalloc(cfg, plan, kv, q, k_new, v_new, out, stream=None):
+    """rkv_decode_step with the library's own split-partial array instead of a
+    workspace (no allocation)."""
+    _check("rkv_decode_step_noalloc",
+           lib().rkv_decode_step_noalloc(ctypes.byref(cfg), _ptr(plan), ctypes.byref(kv),
+                                         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
+                                         _stream(stream)))
 
 
 def rkv_decode_attn_pipelined(cfg, state, plan, plan_next, kv, q, out, workspace=None,

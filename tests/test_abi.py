@@ -416,3 +416,29 @@ def test_tcond_sizes_and_validation(rkv):
     assert mod(c, ctypes.byref(narrow), F, F, F) == rkv.RKV_EINVAL
     assert mod(N, t, F, F, F) == rkv.RKV_EINVAL
     assert rkv.rkv_last_hip_error() == 0
+
+
+def test_no_alloc_step_rejects_what_its_array_cannot_hold(rkv):
+    """rkv_decode_step_noalloc checks every argument, and the size of the split
+    partials against the library's array, before any HIP call."""
+    F, N = ctypes.c_void_p(FAKE), None
+    M = ctypes.c_void_p(MISALIGNED)
+    cfg = good_cfg(rkv)
+    kv = fake_view(rkv)
+    c, k = ctypes.byref(cfg), ctypes.byref(kv)
+    f = rkv.lib().rkv_decode_step_noalloc
+    assert f(c, N, k, F, F, F, F, N) == rkv.RKV_EINVAL
+    assert f(c, F, k, M, F, F, F, N) == rkv.RKV_EALIGN
+    assert f(c, F, k, F, N, F, F, N) == rkv.RKV_EINVAL
+    assert f(N, F, k, F, F, F, F, N) == rkv.RKV_EINVAL
+    # one layer of 64 streams (128 items), 23 splits of a 375-slot ring: 12.2 MB
+    # of partials (128 x 23 x 4,160 bytes) fit ...
+    fits = good_cfg(rkv, num_streams=64, num_layers=1, num_splits=23)
+    assert rkv.rkv_workspace_bytes(fits, 375) == 128 * 23 * 4160
+    assert rkv.rkv_workspace_bytes(fits, 375) < rkv.RKV_NOALLOC_SCRATCH_BYTES
+    # ... 64 splits of an 8192-slot ring (34 MB) do not
+    big = good_cfg(rkv, num_streams=64, num_layers=1, num_splits=64, max_cap=8192)
+    big_kv = fake_view(rkv, slots=8192)
+    assert rkv.rkv_workspace_bytes(big, 8192) > rkv.RKV_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), F, ctypes.byref(big_kv), F, F, F, F, N) == rkv.RKV_ESPACE
+    assert rkv.rkv_last_hip_error() == 0
