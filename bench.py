@@ -885,13 +885,16 @@ def main():
     explicit = args.config is not None
     if args.config is None:
         args.config = 2
+    default_run = not (explicit or args.per_layer or args.tcond or args.kv_fp16 or args.graph
+                       or args.splits or args.layout != "interleaved" or args.path_given)
+    # the other workloads first, so that the headline's timed launches are the
+    # last launches of their kernel in a profile of this command
+    secondary = secondary_runs(args) if default_run and args.secondary else None
     c, res = bench_config(args)
     if args.cpu and not args.kv_fp16 and not args.tcond and not args.per_layer:
         res["cpu_baseline"] = cpu_baseline(c, 1000 + args.config, args.cpu_budget)
-    default_run = not (explicit or args.per_layer or args.tcond or args.kv_fp16 or args.graph
-                       or args.splits or args.layout != "interleaved" or args.path_given)
-    if default_run and args.secondary:
-        res["secondary"] = secondary_runs(args)
+    if secondary is not None:
+        res["secondary"] = secondary
     print(json.dumps(res), flush=True)
 
 
@@ -913,6 +916,7 @@ def secondary_runs(args):
     import torch
     out = {}
     for name, over in SECONDARY:
+        print(f"bench: secondary workload {name}", file=sys.stderr, flush=True)
         a = copy.copy(args)
         a.steps = a.warmup = a.path = None
         for k, v in over.items():
