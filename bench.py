@@ -655,6 +655,52 @@ def device_copy_gbps(mib=1024, reps=10):
     return gbps
 
 
+def _summarize_rocpd(path, root, last, short):
+    """The same figures from rocprofv3's SQLite output (the default format):
+    per-kernel dispatch statistics, the mean of each kernel's last `last`
+    dispatches (in start order), and counter values per dispatch."""
+    import sqlite3
+    from collections import OrderedDict, defaultdict
+    con = sqlite3.connect(path)
+    rel = os.path.relpath(path, root)
+    lines = []
+    dur = defaultdict(list)
+    for name, start, end in con.execute("select name, start, end from kernels order by start"):
+        dur[name].append(int(end) - int(start))
+    if dur:
+        total = sum(sum(d) for d in dur.values())
+        lines.append(f"# rocprofv3 kernel dispatches: {rel}")
+        tail = f" {'last%d_mean_us' % last:>15}" if last else ""
+        lines.append(f"{'calls':>7} {'mean_us':>10} {'median_us':>10} {'min_us':>10} {'max_us':>10} "
+                     f"{'pct':>6}{tail}  kernel")
+        for name, d in sorted(dur.items(), key=lambda x: -sum(x[1])):
+            lt = f" {np.mean(d[-last:]) / 1e3:15.2f}" if last else ""
+            lines.append(f"{len(d):7d} {np.mean(d) / 1e3:10.2f} {np.median(d) / 1e3:10.2f} "
+                         f"{np.min(d) / 1e3:10.2f} {np.max(d) / 1e3:10.2f} "
+                         f"{100.0 * sum(d) / total:6.2f}{lt}  {short(name)}")
+    per = OrderedDict()
+    for name, disp, cname, value in con.execute(
+            "select kernel_name, dispatch_id, counter_name, value from counters_collection "
+            "order by dispatch_id"):
+        per.setdefault((name, disp), defaultdict(float))[cname] += float(value)
+    if per:
+        agg = defaultdict(lambda: defaultdict(list))
+        for (name, _), cnt in per.items():
+            for cn, v in cnt.items():
+                agg[name][cn].append(v)
+        lines.append(f"# counters per dispatch: {rel}")
+        tail = f" {'last%d_mean' % last:>16}" if last else ""
+        lines.append(f"{'dispatches':>10} {'counter':>12} {'mean':>16} {'min':>16} {'max':>16}{tail}"
+                     f"  kernel")
+        for name, cs in agg.items():
+            for cn, v in cs.items():
+                lt = f" {np.mean(v[-last:]):16.1f}" if last else ""
+                lines.append(f"{len(v):10d} {cn:>12} {np.mean(v):16.1f} {np.min(v):16.1f} "
+                             f"{np.max(v):16.1f}{lt}  {short(name)}")
+    con.close()
+    return lines
+
+
 def summarize_rocprof(root, last=0):
     """Per-kernel figures from a rocprofv3 CSV output folder: its own --stats
     table, mean dispatch duration from the kernel trace (and, with last > 0,
@@ -669,6 +715,8 @@ def summarize_rocprof(root, last=0):
         return name if len(name) <= 110 else name[:107] + "..."
 
     lines = []
+    for path in sorted(glob.glob(os.path.join(root, "**", "*.db"), recursive=True)):
+        lines.extend(_summarize_rocpd(path, root, last, short))
     for path in sorted(glob.glob(os.path.join(root, "**", "*_kernel_stats.csv"), recursive=True)):
         lines.append(f"# rocprofv3 --stats: {os.path.relpath(path, root)}")
         lines.append(f"{'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel")

@@ -50,6 +50,8 @@
 // Encoder: each wave writes the new frames that fall in its own tiles before
 // reading them.
 
+#include <stddef.h>
+
 #include <type_traits>
 
 #include "rkv_device.h"
@@ -145,7 +147,7 @@ struct Occupancy {
 template <int D, int NW, int KIND, bool COMP, typename SF>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(Occupancy<D, COMP>::waves)))
-void attn_kernel(AttnArgs a) {
+void attn_kernel(AttnArgs args) {
   constexpr int KS = D / 32;    // k-steps of the score MFMA (32 dims each)
   constexpr int KH = KS / 2;    // k-steps of the first half (pair partner is st + KH)
   constexpr int CW = D / 16;    // V elements per lane per row = probability MFMAs per tile
@@ -161,6 +163,38 @@ void attn_kernel(AttnArgs a) {
   __shared__ f32x4 sm_o[NW > 1 ? NW - 1 : 1][CW][32];  // [wave-1][e][8*g4 + c], c < 8
   __shared__ f32x4 sm_dt[D / 2];  // re-base: hi/lo float32 of cos(D theta_i), -sin(D theta_i)
 
+  // Every argument but the theta table of the plan-advance blocks, copied
+  // up front and pinned in scalar registers, so the argument loads are issued
+  // together and awaited once (fetched at each first use, they cost a round
+  // trip to the argument buffer apiece).
+  AttnArgs a;
+  a.plan = args.plan;
+  a.ring = args.ring;
+  a.q = args.q;
+  a.knew = args.knew;
+  a.vnew = args.vnew;
+  a.out = args.out;
+  a.ws = args.ws;
+  a.S = args.S;
+  a.L = args.L;
+  a.Hkv = args.Hkv;
+  a.G = args.G;
+  a.F = args.F;
+  a.nsplit = args.nsplit;
+  a.out_f32 = args.out_f32;
+  a.scale_log2 = args.scale_log2;
+  a.adv_state = args.adv_state;
+  a.adv_plan = args.adv_plan;
+  a.adv_mode = args.adv_mode;
+  a.adv_dc = args.adv_dc;
+  a.adv_F = args.adv_F;
+  a.adv_half = args.adv_half;
+  asm volatile("" : : "s"(a.plan), "s"(a.ring.k), "s"(a.ring.v), "s"(a.ring.klo), "s"(a.ring.ls),
+               "s"(a.ring.ss), "s"(a.ring.hs), "s"(a.ring.rs), "s"(a.ring.slots));
+  asm volatile("" : : "s"(a.q), "s"(a.knew), "s"(a.vnew), "s"(a.out), "s"(a.ws), "s"(a.S),
+               "s"(a.L), "s"(a.Hkv), "s"(a.G), "s"(a.F), "s"(a.nsplit), "s"(a.out_f32),
+               "s"(a.scale_log2), "s"(a.adv_state));
+
   // Pipelined decode step: the blocks past the attention grid compute the
   // next step's plan, one wave per stream (nothing in this launch reads it).
   if ((KIND == kDecodeFused || KIND == kDecodeRead) && a.adv_state) {
@@ -169,7 +203,7 @@ void attn_kernel(AttnArgs a) {
       const int s = ((int)blockIdx.x - njobs) * NW + (int)(threadIdx.x >> 6);
       if (s < a.S)
         advance_stream(a.adv_state, a.adv_plan, s, threadIdx.x & 63, a.adv_mode, a.adv_dc,
-                       a.adv_F, a.adv_half, a.adv_theta);
+                       a.adv_F, a.adv_half, args.adv_theta);
       return;
     }
   }
@@ -188,14 +222,22 @@ void attn_kernel(AttnArgs a) {
   const int s = (item / a.Hkv) % a.S;
   const int l = item / (a.Hkv * a.S);
   const rkv_step_plan* P = a.plan + s;
+  // The plan header (t, pos, first_pos, slot, n_valid, rebase_delta, cap,
+  // new_rows) is requested with the other set-up loads and read only after
+  // the first tiles are requested, so that no load waits for it.
+  // (Only words that are used are loaded: a load whose destination holds a
+  // dead word makes the next writer of that register wait for it.)
+  const char* phb = reinterpret_cast<const char*>(P);
+  const u32x4 hd0 = *reinterpret_cast<const u32x4*>(phb);                         // t, pos
+  const u32x2 hd1 = *reinterpret_cast<const u32x2*>(phb + offsetof(rkv_step_plan, first_pos));
+  const u32x2 hd2 = *reinterpret_cast<const u32x2*>(phb + offsetof(rkv_step_plan, slot));
+  const uint32_t hd3 = *reinterpret_cast<const uint32_t*>(phb +
+                                                          offsetof(rkv_step_plan, rebase_delta));
+  const u32x2 hd4 = *reinterpret_cast<const u32x2*>(phb + offsetof(rkv_step_plan, cap));
 
   const int slots = a.ring.slots;
   const int per = (((slots + a.nsplit - 1) / a.nsplit) + TK - 1) & ~(TK - 1);
   const int kb = split * per;
-  // n_valid <= cap <= slots is guaranteed by the host checks; the clamp only
-  // bounds the reads of a corrupted plan
-  const int n_valid = P->n_valid < slots ? P->n_valid : slots;
-  const int ke = kb + per < n_valid ? kb + per : n_valid;
 
   const int64_t rbase = (int64_t)l * a.ring.ls + (int64_t)s * a.ring.ss + (int64_t)g * a.ring.hs;
   uint16_t* __restrict__ Kp = a.ring.k + rbase;
@@ -290,6 +332,14 @@ void attn_kernel(AttnArgs a) {
     }
     vnew_c = VC::load(a.vnew + new_off(0) + CW * c);
   }
+  // The re-base angle's float64 cos/sin (used only when the base moves; wave
+  // 0 turns them into the float32 tables), requested with the set-up loads.
+  double dt_c = 1.0, dt_s = 0.0;
+  if (KIND == kDecodeFused && wave == 0) {
+    const int i = lane < D / 2 ? lane : 0;
+    dt_c = P->rope_delta[0][i];
+    dt_s = P->rope_delta[1][i];
+  }
   // keep the tile loads behind the set-up loads in issue order
   __builtin_amdgcn_sched_barrier(0);
   const int first = kb + TK * wave;
@@ -297,6 +347,29 @@ void attn_kernel(AttnArgs a) {
   Tile tb[2];
   load_tile(first, tb[0], kalloc - 1 > 0 ? kalloc - 1 : 0);
   load_tile(first + TK * NW, tb[1], kalloc - 1 > 0 ? kalloc - 1 : 0);
+  // everything above is requested before anything below waits for data
+  __builtin_amdgcn_sched_barrier(0);
+
+  // plan header fields (uniform: read from the first lane)
+  const int64_t plan_t = ((int64_t)__builtin_amdgcn_readfirstlane(hd0[1]) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane(hd0[0]);
+  const int64_t plan_pos = ((int64_t)__builtin_amdgcn_readfirstlane(hd0[3]) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane(hd0[2]);
+  const int64_t first_pos = ((int64_t)__builtin_amdgcn_readfirstlane(hd1[1]) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane(hd1[0]);
+  const int slot_new = __builtin_amdgcn_readfirstlane(hd2[0]);
+  const int plan_n_valid = __builtin_amdgcn_readfirstlane(hd2[1]);
+  const int plan_delta = __builtin_amdgcn_readfirstlane(hd3);
+  const int cap = __builtin_amdgcn_readfirstlane(hd4[0]);
+  const int nnew = __builtin_amdgcn_readfirstlane(hd4[1]);
+  static_assert(offsetof(rkv_step_plan, pos) == 8 &&
+                    offsetof(rkv_step_plan, n_valid) == offsetof(rkv_step_plan, slot) + 4 &&
+                    offsetof(rkv_step_plan, new_rows) == offsetof(rkv_step_plan, cap) + 4,
+                "plan header layout");
+  // n_valid <= cap <= slots is guaranteed by the host checks; the clamp only
+  // bounds the reads of a corrupted plan
+  const int n_valid = plan_n_valid < slots ? plan_n_valid : slots;
+  const int ke = kb + per < n_valid ? kb + per : n_valid;
 
 #pragma unroll
   for (int k = 0; k < UPW; ++k) {
@@ -320,10 +393,7 @@ void attn_kernel(AttnArgs a) {
   }
 
   // ---- fused-update parameters ----
-  const int delta = (KIND == kDecodeFused) ? P->rebase_delta : 0;
-  const int slot_new = P->slot;
-  const int nnew = P->new_rows;
-  const int cap = P->cap;
+  const int delta = (KIND == kDecodeFused) ? plan_delta : 0;
 
   auto new_index = [&](int row) -> int {
     if (KIND == kDecodeFused) return row == slot_new ? 0 : -1;
@@ -392,9 +462,12 @@ void attn_kernel(AttnArgs a) {
       const uint32_t w1 = SF::cvt2_f64(y1[0], y1[1]);
       const uint32_t w2 = SF::cvt2_f64(y2[0], y2[1]);
       if (c == 0) {
-        const int o = 32 * st + 8 * g4 + 2 * w;
         reinterpret_cast<uint32_t*>(&sm_newk[st][g4])[w] = w1;
         reinterpret_cast<uint32_t*>(&sm_newk[st + KH][g4])[w] = w2;
+      }
+      // every split keeps the new row in LDS; split 0 writes it to the ring
+      if (c == 0 && split == 0) {
+        const int o = 32 * st + 8 * g4 + 2 * w;
         *reinterpret_cast<uint32_t*>(Kp + slot_new * rs + o) = w1;
         *reinterpret_cast<uint32_t*>(Kp + slot_new * rs + o + 32 * KH) = w2;
         if (COMP) {
@@ -408,7 +481,7 @@ void attn_kernel(AttnArgs a) {
     if (wave == NW - 1 && g4 == 0) {
       const VT vs = VC::template from_input<SF>(vnew_c);
       sm_newv[c] = vs;
-      VC::store(Vp + slot_new * rs + CW * c, vs);
+      if (split == 0) VC::store(Vp + slot_new * rs + CW * c, vs);
     }
   }
 
@@ -446,18 +519,16 @@ void attn_kernel(AttnArgs a) {
   }
 
   // Re-base tables for the in-loop rotation (float32, from the float64 plan).
-  if (KIND == kDecodeFused && delta != 0 && wave == 0) {
-    for (int i = lane; i < D / 2; i += 64)
-      sm_dt[i] = rebase_table_entry(P->rope_delta[0][i], P->rope_delta[1][i]);
-  }
+  static_assert(D / 2 <= 64, "one rotary pair per lane of wave 0");
+  if (KIND == kDecodeFused && delta != 0 && wave == 0 && lane < D / 2)
+    sm_dt[lane] = rebase_table_entry(dt_c, dt_s);
 
   __syncthreads();  // the query operand (and the decoder's new row) is in LDS
 
   // encoder mask bookkeeping
-  const int64_t last_pos = P->t;
+  const int64_t last_pos = plan_t;
   const int slot_last = (slot_new + nnew - 1) % cap;
-  const int64_t first_pos = P->first_pos;
-  const int64_t qpos = P->pos + col_q;
+  const int64_t qpos = plan_pos + col_q;
 
   float m_run = -INFINITY;
   float l_run = 0.f;
