@@ -13,11 +13,14 @@
 // output feature, contiguous in k) is the A operand and the activations (row
 // = token) the B operand, so a lane's result holds four consecutive output
 // features of one token and the epilogue writes them as one vector.  A
-// workgroup computes 64 tokens x 64 features: both 64 x 64 operand tiles of a
+// workgroup computes 64 tokens x 64 features: both operand tiles of a
 // k-stage are staged through LDS (double-buffered; the global loads of the
 // next kDepth stages are in flight during a stage's MFMAs), and each of the 4
 // waves computes a 32 x 32 quarter from them, so every loaded element feeds
-// 64 products instead of 16.
+// 64 products instead of 16.  Two workgroups share a CU (two waves per
+// SIMD): a 64 x 128 tile (one workgroup per CU at 512 tokens, 0.75 instead of
+// one operand read per product) measured slower, its single wave per SIMD
+// left with nothing to run while it waits for LDS.
 
 #include <math.h>
 
@@ -45,13 +48,26 @@ __device__ __forceinline__ float gelu_erf(float x) {
 }
 
 constexpr int kTM = 64, kTN = 64, kKS = 64;
-constexpr int kLdk = kKS + 8;      // LDS row stride (elements): 144 B, rows rotate banks
+// LDS tiles: rows of kKS elements (128 bytes) without padding; the eight
+// 16-byte chunks of row r are stored in the order chunk ^ ((r >> 1) & 7).
+// A 16-lane group of a 16-byte operand read takes one chunk of 16
+// consecutive rows and a group of a staging write two whole rows: either
+// way the swizzle puts the 16 pieces on 16 distinct 4-bank groups of the 64
+// banks.  (Rows padded to 144 bytes left the staging writes 2-way conflicted:
+// the bank-conflict counter read as many cycles as LDS instructions were
+// active.)
+__device__ __forceinline__ int lds_at(int row, int chunk) {
+  return row * kKS + 8 * (chunk ^ ((row >> 1) & 7));
+}
 constexpr int kDepth = 2;          // k-stages whose global loads are in flight
+constexpr int kWF = kTN / 2;       // features per wave (2 x 2 waves: 32 tokens x 32 features)
+constexpr int kFB = kWF / 16;      // 16-feature MFMA blocks per wave
+constexpr int kWRows = kTN / 32;   // weight rows each thread stages per k-stage
 
 template <int EP>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmSet set, int M, int N, int K, int ld) {
-  __shared__ __attribute__((aligned(16))) uint16_t sw[2][kTN * kLdk];
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTM * kLdk];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[2][kTN * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTM * kKS];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -60,64 +76,76 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmSet set, int M, int N, in
   const uint16_t* __restrict__ w = set.w[blockIdx.z];
   const uint16_t* __restrict__ x = set.x[blockIdx.z];
   const int n0 = blockIdx.x * kTN, m0 = blockIdx.y * kTM;
-  // staging: thread t moves the 16-byte pieces (row t/8 and 32 + t/8, k 8 (t%8))
-  // of both tiles; token rows past M are clamped (read, never stored)
+  // staging: thread t moves the 16-byte pieces (row t/8 + 32 r, k 8 (t%8)) of
+  // both tiles; token rows past M and feature rows past N (N is a multiple of
+  // 64, so a last tile may hold 64 features) are clamped: read, never stored
   const int lr = t >> 3, lk = 8 * (t & 7);
-  const uint16_t* wp0 = w + (int64_t)(n0 + lr) * ld + lk;
-  const uint16_t* wp1 = wp0 + (int64_t)32 * ld;
+  const uint16_t* wp[kWRows];
+#pragma unroll
+  for (int r = 0; r < kWRows; ++r) wp[r] = w + (int64_t)min(n0 + 32 * r + lr, N - 1) * ld + lk;
   const uint16_t* xp0 = x + (int64_t)min(m0 + lr, M - 1) * ld + lk;
   const uint16_t* xp1 = x + (int64_t)min(m0 + 32 + lr, M - 1) * ld + lk;
   const int steps = K / kKS;
   // register ring: stage s's pieces sit in slot s % kDepth from its load until
   // its LDS store, which frees the slot for stage s + kDepth
-  u32x4 rw0[kDepth], rw1[kDepth], rx0[kDepth], rx1[kDepth];
+  u32x4 rw[kDepth][kWRows], rx0[kDepth], rx1[kDepth];
   auto gload = [&](int s, int slot) {
     const int k0 = (s < steps ? s : steps - 1) * kKS;   // past the end: a harmless reload
-    rw0[slot] = ld16(wp0 + k0);
-    rw1[slot] = ld16(wp1 + k0);
+#pragma unroll
+    for (int r = 0; r < kWRows; ++r) rw[slot][r] = ld16(wp[r] + k0);
     rx0[slot] = ld16(xp0 + k0);
     rx1[slot] = ld16(xp1 + k0);
   };
   auto lstore = [&](int b, int slot) {
-    *reinterpret_cast<u32x4*>(&sw[b][lr * kLdk + lk]) = rw0[slot];
-    *reinterpret_cast<u32x4*>(&sw[b][(32 + lr) * kLdk + lk]) = rw1[slot];
-    *reinterpret_cast<u32x4*>(&sx[b][lr * kLdk + lk]) = rx0[slot];
-    *reinterpret_cast<u32x4*>(&sx[b][(32 + lr) * kLdk + lk]) = rx1[slot];
+    const int ch = lk >> 3;
+#pragma unroll
+    for (int r = 0; r < kWRows; ++r)
+      *reinterpret_cast<u32x4*>(&sw[b][lds_at(32 * r + lr, ch)]) = rw[slot][r];
+    *reinterpret_cast<u32x4*>(&sx[b][lds_at(lr, ch)]) = rx0[slot];
+    *reinterpret_cast<u32x4*>(&sx[b][lds_at(32 + lr, ch)]) = rx1[slot];
   };
-  f32x4 acc[2][2];
+  f32x4 acc[2][kFB];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kFB; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // operand fragments of one 32-k chunk: the next chunk's are read from LDS
+  // before this chunk's products are issued, so the LDS latency hides behind
+  // them (read and used at once, the wave waits for every read)
+  auto frag = [&](int b, int kk, bf16x8* fa, bf16x8* fb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kFB; ++i)
+      fa[i] = __builtin_bit_cast(
+          bf16x8,
+          *reinterpret_cast<const u32x4*>(&sw[b][lds_at(wn * kWF + 16 * i + c, (kk >> 3) + g)]));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      fb[j] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(&sx[b][lds_at(wm * 32 + 16 * j + c, (kk >> 3) + g)]));
+  };
+  auto mma = [&](const bf16x8* fa, const bf16x8* fb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < kFB; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[j][i], 0, 0, 0);
+  };
+  static_assert(kKS == 64, "a k-stage is two 32-k chunks");
+  bf16x8 fa0[kFB], fb0[2], fa1[kFB], fb1[2];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) gload(d, d);
   lstore(0, 0);
   gload(kDepth, 0);
   __syncthreads();
+  frag(0, 0, fa0, fb0);
   for (int s0 = 0; s0 < steps; s0 += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
       const int s = s0 + u;
       if (s < steps) {
         const int b = u & 1;                            // kDepth even: s & 1
-#pragma unroll
-        for (int kk = 0; kk < kKS; kk += 32) {
-          bf16x8 fa[2], fb[2];
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            fa[i] = __builtin_bit_cast(
-                bf16x8,
-                *reinterpret_cast<const u32x4*>(&sw[b][(wn * 32 + 16 * i + c) * kLdk + kk + 8 * g]));
-            fb[i] = __builtin_bit_cast(
-                bf16x8,
-                *reinterpret_cast<const u32x4*>(&sx[b][(wm * 32 + 16 * i + c) * kLdk + kk + 8 * g]));
-          }
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-              acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[j][i], 0, 0, 0);
-        }
+        frag(b, 32, fa1, fb1);
+        mma(fa0, fb0);
         // the LDS buffer written here was last read in stage s - 1, which every
         // wave finished before the barrier that ended it
         if (s + 1 < steps) {
@@ -125,20 +153,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmSet set, int M, int N, in
           lstore(b ^ 1, slot);
           if (s + 1 + kDepth < steps) gload(s + 1 + kDepth, slot);
         }
+        mma(fa1, fb1);
         __syncthreads();
+        if (s + 1 < steps) frag(b ^ 1, 0, fa0, fb0);
       }
     }
   }
-  // lane (c, g) of acc[j][i] holds features n0 + 32 wn + 16 i + 4 g + r, r < 4,
+  // lane (c, g) of acc[j][i] holds features n0 + kWF wn + 16 i + 4 g + r, r < 4,
   // of token m0 + 32 wm + 16 j + c
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int m = m0 + 32 * wm + 16 * j + c;
     if (m >= M) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kFB; ++i) {
       const f32x4 v = acc[j][i];
-      const int n = n0 + 32 * wn + 16 * i + 4 * g;
+      const int n = n0 + kWF * wn + 16 * i + 4 * g;
+      if (n >= N) continue;
       if (EP == kAddF32) {
         float* p = reinterpret_cast<float*>(set.c[blockIdx.z]) + (int64_t)m * N + n;
         const f32x4 old = *reinterpret_cast<const f32x4*>(p);
@@ -258,7 +289,7 @@ hipError_t launch_gemm(GemmEpilogue ep, const uint16_t* const* w, const uint16_t
     set.x[i] = x[i];
     set.c[i] = c[i];
   }
-  const dim3 grid(N / kTN, (M + kTM - 1) / kTM, count);
+  const dim3 grid((N + kTN - 1) / kTN, (M + kTM - 1) / kTM, count);
   switch (ep) {
     case GemmEpilogue::kStoreBf16:
       hipLaunchKernelGGL((gemm_kernel<kStoreBf16>), grid, dim3(256), 0, stream, set, M, N, K, ld);
