@@ -138,9 +138,13 @@ def launch_bytes(c, windows, origins, steps):
     return total * L
 
 
-def kernel_source_digest():
+ATTN_SOURCES = ("attn.hip", "rkv_device.h", "rkv_internal.h", "rkv_plan.h")
+
+
+def kernel_source_digest(files=ATTN_SOURCES):
+    """Digest of the kernel sources a stored counter figure was taken from."""
     h = hashlib.sha256()
-    for name in ("attn.hip", "rkv_device.h", "rkv_internal.h"):
+    for name in files:
         with open(os.path.join(ROOT, "rolling_window_kv_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -155,7 +159,8 @@ def load_traffic(kernel, workload):
     except (OSError, ValueError):
         return None
     ent = data.get(f"{kernel}@{workload}")
-    if not ent or ent.get("kernel_src_digest") != kernel_source_digest():
+    files = tuple(ent.get("kernel_src_files", ATTN_SOURCES)) if ent else ATTN_SOURCES
+    if not ent or ent.get("kernel_src_digest") != kernel_source_digest(files):
         return None
     return ent.get("hbm_bytes_per_launch")
 

@@ -55,7 +55,8 @@ def test_committed_hbm_counters_are_reported_only_for_their_kernel_sources():
     for key, ent in data.items():
         kernel, workload = key.rsplit("@", 1)
         got = b.load_traffic(kernel, workload)
-        if ent["kernel_src_digest"] == b.kernel_source_digest():
+        files = tuple(ent.get("kernel_src_files", b.ATTN_SOURCES))
+        if ent["kernel_src_digest"] == b.kernel_source_digest(files):
             assert got == ent["hbm_bytes_per_launch"], key
         else:
             assert got is None, key
