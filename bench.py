@@ -291,6 +291,8 @@ def run_gpu(c, args):
     t_setup = time.perf_counter()
     q, k, v = build_inputs(c, seed, dev)
     kv_flags = rkv.RKV_F_KV_FP16 if args.kv_fp16 else 0
+    if args.merge_launch:
+        kv_flags |= rkv.RKV_F_MERGE_LAUNCH
     if c["mode"] == "rebase":
         flags = (rkv.RKV_F_COMPENSATED if c.get("comp") else 0) | kv_flags
         cfg = rkv.make_cfg(S, L, rebase_chunk=c["dc"], flags=flags, num_splits=args.splits)
@@ -344,7 +346,7 @@ def run_gpu(c, args):
                              None if cache.k_lo is None else cache.k_lo[l:l + 1])
                  for l in range(L)]
         nb = rkv.rkv_workspace_bytes(cfg1, cache.k.shape[3])
-        ws1 = torch.empty((nb + 3) // 4, dtype=torch.float32, device=dev) if nb else None
+        ws1 = torch.zeros((nb + 3) // 4, dtype=torch.float32, device=dev) if nb else None
         slices = [[(q[j][l], k[j][l], v[j][l]) for l in range(L)] for j in range(q.shape[0])]
         outs = [out[l] for l in range(L)]
         per_layer = (cfg1, views, ws1, slices, outs)
@@ -889,6 +891,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, metavar="N",
                     help="key-range splits per (layer, stream, head) of the attention "
                          "launches (0: the library's choice)")
+    ap.add_argument("--merge-launch", action="store_true",
+                    help="merge split key ranges in a second launch (RKV_F_MERGE_LAUNCH) "
+                         "instead of inside the attention launch")
     ap.add_argument("--graph", action="store_true",
                     help="with --per-layer: replay each step as a captured HIP graph")
     ap.add_argument("--layout", choices=("interleaved", "separate"), default="interleaved",

@@ -95,7 +95,15 @@ enum {
    * or, for V, from the bfloat16 input); q, k_new, v_new stay bfloat16 and
    * the matrix-core products run in fp16.  REBASE and COMPACT modes only
    * (RKV_EUNSUPPORTED for ENC_CHUNK). */
-  RKV_F_KV_FP16 = 1u << 2
+  RKV_F_KV_FP16 = 1u << 2,
+  /* When a call splits the key range (rkv_workspace_bytes() > 0), always
+   * merge the splits' partial results in a second launch (same results, bit
+   * for bit).  Without it, a split launch of at most 768 workgroups (items x
+   * splits: one round on the chip) merges in the attention launch itself --
+   * the last split of each (layer, stream, head) to finish merges, counted by
+   * per-item counters in the workspace, which must then be zero at the first
+   * call -- and larger ones in a second launch. */
+  RKV_F_MERGE_LAUNCH = 1u << 3
 };
 
 /* Problem description, shared by every call of a step (host memory). */
@@ -206,7 +214,12 @@ int rkv_state_init(const rkv_cfg* cfg, rkv_stream_state* d_state, const int32_t*
 
 /* Bytes of workspace rkv_decode_attn / rkv_decode_step /
  * rkv_encoder_chunk_attn need for a cache of `slots` rows per head (0 when
- * the key range is not split). */
+ * the key range is not split).  Layout: one uint32 merge counter per
+ * (layer, stream, kv head) item, padded to 256 bytes, then the float32 split
+ * partials.  Unless cfg has RKV_F_MERGE_LAUNCH the counters must be zero when
+ * a call starts: zero-fill a new workspace before its first use (and after
+ * using it with another configuration); every call leaves them zero when its
+ * launch completes. */
 size_t rkv_workspace_bytes(const rkv_cfg* cfg, int32_t slots);
 
 /* Step plan (Audio8 explainer "Rolling KV Cache 三步拆解" steps 1-2; voxtral.c
@@ -284,10 +297,14 @@ int rkv_decode_step(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
  * make one call before capturing a graph.  The current device must be the
  * one hip_stream belongs to.  Every call on a GPU shares that GPU's array
  * and leaves its contents behind; calls whose launches may overlap in time on
- * one GPU (unordered streams) race and give wrong results.  Errors as
- * rkv_decode_step, and RKV_ESPACE when rkv_workspace_bytes(cfg, kv->slots)
- * exceeds RKV_NOALLOC_SCRATCH_BYTES (checked before any HIP call). */
+ * one GPU (unordered streams) race and give wrong results.  The array ends
+ * in RKV_NOALLOC_MAX_SPLIT_ITEMS merge counters (zero at load; every call
+ * leaves them zero), the rest holds the split partials.  Errors as
+ * rkv_decode_step, and RKV_ESPACE when a split call's partials (the
+ * workspace minus its counters) exceed the rest of the array or it has more
+ * than RKV_NOALLOC_MAX_SPLIT_ITEMS items (checked before any HIP call). */
 #define RKV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+#define RKV_NOALLOC_MAX_SPLIT_ITEMS 16384 /* items of a split call; counters at the array's end */
 int rkv_decode_step_noalloc(const rkv_cfg* cfg, const rkv_step_plan* d_plan,
                             const rkv_kv_view* kv, const void* q, const void* k_new,
                             const void* v_new, void* out, void* hip_stream);

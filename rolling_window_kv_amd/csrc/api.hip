@@ -30,7 +30,8 @@ int check_cfg(const rkv_cfg* c) {
     return RKV_EINVAL;
   if (c->head_dim != 64 && c->head_dim != 128) return RKV_EUNSUPPORTED;
   if (c->mode < RKV_MODE_REBASE || c->mode > RKV_MODE_ENC_CHUNK) return RKV_EUNSUPPORTED;
-  if (c->flags & ~(uint32_t)(RKV_F_COMPENSATED | RKV_F_OUT_F32 | RKV_F_KV_FP16))
+  if (c->flags &
+      ~(uint32_t)(RKV_F_COMPENSATED | RKV_F_OUT_F32 | RKV_F_KV_FP16 | RKV_F_MERGE_LAUNCH))
     return RKV_EUNSUPPORTED;
   if (!(c->rope_base > 0.0) || !isfinite(c->rope_base)) return RKV_EINVAL;
   if (!(c->softmax_scale >= 0.0f) || !isfinite(c->softmax_scale)) return RKV_EINVAL;
@@ -97,18 +98,33 @@ rkv::RingArgs ring_of(const rkv_kv_view* kv) {
   return r;
 }
 
-size_t workspace_for(const rkv_cfg* c, int32_t slots) {
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace of a split launch: one merge counter per item (zero between
+// calls), then the float32 partials [item][split][16 + 8 d].
+size_t ticket_bytes(const rkv_cfg* c) {
+  return align256((size_t)c->num_layers * c->num_streams * c->num_kv_heads * sizeof(uint32_t));
+}
+size_t partial_bytes(const rkv_cfg* c, int32_t slots) {
   const int n = rkv::choose_splits(c, slots);
   if (n <= 1) return 0;
   const int64_t items = (int64_t)c->num_layers * c->num_streams * c->num_kv_heads;
   return (size_t)(items * n * rkv::partial_floats(c->head_dim) * (int64_t)sizeof(float));
+}
+size_t workspace_for(const rkv_cfg* c, int32_t slots) {
+  const size_t p = partial_bytes(c, slots);
+  return p ? ticket_bytes(c) + p : 0;
 }
 
 // Device array for the allocation-free entry point: each GPU the library
 // runs on holds its own copy until the process ends.  Host code never uses
 // the array's name as an address (in host code it is only a stand-in): the
 // device address comes from hipGetSymbolAddress, looked up once per device.
+// Its last kScratchTicketBytes hold the merge counters (one per item, zero
+// at load and after every call), the rest the split partials, so counters
+// never land where an earlier call with another configuration left partials.
 constexpr size_t kScratchBytes = RKV_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kScratchTicketBytes = (size_t)RKV_NOALLOC_MAX_SPLIT_ITEMS * sizeof(uint32_t);
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -158,13 +174,26 @@ int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
   if ((rc = check_ptr(q)) || (rc = check_ptr(out))) return rc;
   if (kind != rkv::kDecodeRead && ((rc = check_ptr(knew)) || (rc = check_ptr(vnew)))) return rc;
   const size_t need = workspace_for(cfg, kv->slots);
+  float* partials = nullptr;
+  uint32_t* tickets = nullptr;
   if (ws == kUseScratch) {
-    if (need > kScratchBytes) return RKV_ESPACE;
-    ws = nullptr;
-    if (need && (rc = scratch_address(&ws))) return rc;
+    const size_t pbytes = partial_bytes(cfg, kv->slots);
+    const int64_t items = (int64_t)cfg->num_layers * cfg->num_streams * cfg->num_kv_heads;
+    if (pbytes &&
+        (pbytes > kScratchBytes - kScratchTicketBytes || items > RKV_NOALLOC_MAX_SPLIT_ITEMS))
+      return RKV_ESPACE;
+    void* base = nullptr;
+    if (pbytes && (rc = scratch_address(&base))) return rc;
+    if (pbytes) {
+      partials = static_cast<float*>(base);
+      tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(base) + kScratchBytes -
+                                            kScratchTicketBytes);
+    }
   } else if (need) {
     if (!ws || ws_bytes < need) return RKV_ESPACE;
     if (!aligned16(ws)) return RKV_EALIGN;
+    tickets = static_cast<uint32_t*>(ws);
+    partials = reinterpret_cast<float*>(static_cast<char*>(ws) + ticket_bytes(cfg));
   }
   rkv::AttnArgs a;
   a.plan = plan;
@@ -173,13 +202,23 @@ int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
   a.knew = static_cast<const uint16_t*>(knew);
   a.vnew = static_cast<const uint16_t*>(vnew);
   a.out = out;
-  a.ws = static_cast<float*>(ws);
+  a.ws = partials;
+  a.nsplit = rkv::choose_splits(cfg, kv->slots);
+  // The splits merge inside the attention launch when its workgroups fit in
+  // one round on the chip (latency-bound launches: one layer, few streams);
+  // a launch of several rounds merges in a second launch, because there the
+  // waves that wait for the hand-over hold slots other workgroups would
+  // stream in (26 x 16 compaction, 3 splits: 589 against 562 us a step).
+  const int64_t blocks = (int64_t)cfg->num_layers * cfg->num_streams * cfg->num_kv_heads *
+                         a.nsplit;
+  a.tickets = ((cfg->flags & RKV_F_MERGE_LAUNCH) || blocks > rkv::kMergeInLaunchMaxBlocks)
+                  ? nullptr
+                  : tickets;
   a.S = cfg->num_streams;
   a.L = cfg->num_layers;
   a.Hkv = cfg->num_kv_heads;
   a.G = kind == rkv::kEncoderFused ? cfg->new_rows : cfg->num_q_heads / cfg->num_kv_heads;
   a.F = cfg->new_rows;
-  a.nsplit = rkv::choose_splits(cfg, kv->slots);
   a.out_f32 = (cfg->flags & RKV_F_OUT_F32) ? 1 : 0;
   const double scale =
       cfg->softmax_scale > 0.0f ? (double)cfg->softmax_scale : 1.0 / sqrt((double)cfg->head_dim);
@@ -479,7 +518,6 @@ static size_t encoder_layer_elems(const rkv_cfg* cfg, const rkv_encoder_cfg* ec)
   return 2 * h + 4 * h * h + 2 * h * f;
 }
 
-static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t rkv_encoder_layer_weight_bytes(const rkv_cfg* cfg, const rkv_encoder_cfg* ec) {
   if (check_encoder(cfg, ec)) return 0;
@@ -537,6 +575,9 @@ int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_st
   const int64_t part_stride = (int64_t)M * H;
   rkv_cfg one = *cfg;
   one.num_layers = 1;
+  // split partials (few streams) merged by a second launch: the merge
+  // counters of an in-launch merge would need a zeroed workspace
+  one.flags |= RKV_F_MERGE_LAUNCH;
   const size_t layer_elems = encoder_layer_elems(cfg, ec);
   const int so = encoder_splits(H), s2 = encoder_splits(FF);
   hipError_t e;

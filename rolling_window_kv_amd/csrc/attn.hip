@@ -144,6 +144,66 @@ struct Occupancy {
   static constexpr int waves = D == 128 && COMP ? 2 : 3;
 };
 
+// Merge of an item's split partials by the last split to finish, in the
+// attention launch:  out = sum_j 2^(m_j - M) num_j / sum_j 2^(m_j - M) l_j,
+// M = max_j m_j, the sums taken over the splits in order -- the arithmetic of
+// combine_kernel, so the two merges give the same bits.  Thread `tid` of NT
+// takes the output quads tid, tid + NT, ... (head hh, dims dd .. dd + 3); the
+// partials are read with device-scope loads (pb covers the item's partials),
+// up to 8 splits in flight.  `base` is the output offset of head 0 and
+// `hstride` the distance between heads.
+template <int D, int NT>
+__device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t pb, const AttnArgs& a,
+                                               int64_t base, int64_t hstride, int tid) {
+  const int ns = a.nsplit;
+  const int pf = (int)partial_floats(D);
+  const int nq = a.G * (D / 4);
+  for (int qd = tid; qd < nq; qd += NT) {
+    const int hh = qd / (D / 4);
+    const int dd = 4 * (qd - hh * (D / 4));
+    float m8[8], l8[8];
+    f32x4 v8[8];
+    auto fetch = [&](int j0) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u < ns ? j0 + u : ns - 1;  // clamped: read, never used
+        m8[u] = ld_dev(pb, 4 * (j * pf + hh));
+        l8[u] = ld_dev(pb, 4 * (j * pf + 8 + hh));
+        v8[u] = ld_dev4(pb, 4 * (j * pf + 16 + hh * D + dd));
+      }
+    };
+    fetch(0);
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < ns) M = fmaxf(M, m8[u]);
+    for (int j = 8; j < ns; ++j) M = fmaxf(M, ld_dev(pb, 4 * (j * pf + hh)));
+    float den = 0.f;
+    f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < ns; j0 += 8) {
+      if (j0 > 0) fetch(j0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < ns) {
+          const float f = (M == -INFINITY || m8[u] == -INFINITY) ? 0.f : fast_exp2(m8[u] - M);
+          den += f * l8[u];
+          num += f * v8[u];
+        }
+      }
+    }
+    float o4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o4[k] = den > 0.f ? num[k] / den : 0.f;
+    const int64_t off = base + hh * hstride + dd;
+    if (a.out_f32)
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) =
+          f32x4{o4[0], o4[1], o4[2], o4[3]};
+    else
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + off) =
+          u32x2{f2bf(o4[0]) | (f2bf(o4[1]) << 16), f2bf(o4[2]) | (f2bf(o4[3]) << 16)};
+  }
+}
+
 template <int D, int NW, int KIND, bool COMP, typename SF>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(Occupancy<D, COMP>::waves)))
@@ -175,6 +235,7 @@ void attn_kernel(AttnArgs args) {
   a.vnew = args.vnew;
   a.out = args.out;
   a.ws = args.ws;
+  a.tickets = args.tickets;
   a.S = args.S;
   a.L = args.L;
   a.Hkv = args.Hkv;
@@ -193,7 +254,7 @@ void attn_kernel(AttnArgs args) {
                "s"(a.ring.ss), "s"(a.ring.hs), "s"(a.ring.rs), "s"(a.ring.slots));
   asm volatile("" : : "s"(a.q), "s"(a.knew), "s"(a.vnew), "s"(a.out), "s"(a.ws), "s"(a.S),
                "s"(a.L), "s"(a.Hkv), "s"(a.G), "s"(a.F), "s"(a.nsplit), "s"(a.out_f32),
-               "s"(a.scale_log2), "s"(a.adv_state));
+               "s"(a.scale_log2), "s"(a.adv_state), "s"(a.tickets));
 
   // Pipelined decode step: the blocks past the attention grid compute the
   // next step's plan, one wave per stream (nothing in this launch reads it).
@@ -679,6 +740,9 @@ void attn_kernel(AttnArgs args) {
     for (int r = 0; r < 4; ++r) oacc[e][r] += dpp_ror8(oacc[e][r]);
 
   // ---- merge the waves in wave 0 ----
+  // When the item's key range is split and the splits merge in this launch,
+  // every wave stays for the hand-over (the last split's waves all merge).
+  const bool merge_here = a.nsplit > 1 && a.tickets != nullptr;
   if (NW > 1) {
     if (wave > 0 && c < 8) {
       if (g4 == 0) {
@@ -689,8 +753,8 @@ void attn_kernel(AttnArgs args) {
       for (int e = 0; e < CW; ++e) sm_o[wave - 1][e][8 * g4 + c] = oacc[e];
     }
     __syncthreads();
-    if (wave > 0) return;
-    if (c < 8) {
+    if (wave > 0 && !merge_here) return;
+    if (wave == 0 && c < 8) {
       float M = m_run;
 #pragma unroll
       for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][c]);
@@ -709,11 +773,10 @@ void attn_kernel(AttnArgs args) {
       m_run = M;
     }
   }
-  if (c >= 8) return;
 
   // ---- output (or split partial): dims [4*CW*g4, 4*CW*g4 + 4*CW) of column c ----
   const int h = c;
-  if (h >= a.G) return;
+  const bool writer = wave == 0 && c < 8 && h < a.G;
   float o[4 * CW];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -721,6 +784,7 @@ void attn_kernel(AttnArgs args) {
     for (int e = 0; e < CW; ++e) o[CW * r + e] = oacc[e][r];
   const int d0 = 4 * CW * g4;
   if (a.nsplit == 1) {
+    if (!writer) return;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const int64_t off = vec_off(h) + d0;
     if (a.out_f32) {
@@ -740,8 +804,14 @@ void attn_kernel(AttnArgs args) {
         st16(op + 8 * q8, w);
       }
     }
-  } else {
-    float* pp = a.ws + ((int64_t)item * a.nsplit + split) * partial_floats(D);
+    return;
+  }
+  // Split partial: maxima [0, 8), sums [8, 16), numerators [16 + h*D + dim).
+  const int64_t pf = partial_floats(D);
+  float* ib = a.ws + (int64_t)item * a.nsplit * pf;  // this item's partials
+  if (!merge_here) {
+    if (!writer) return;
+    float* pp = ib + split * pf;
     if (g4 == 0) {
       pp[h] = m_run;
       pp[8 + h] = l_run;
@@ -750,7 +820,37 @@ void attn_kernel(AttnArgs args) {
     for (int q4 = 0; q4 < CW; ++q4)
       *reinterpret_cast<f32x4*>(pp + 16 + h * D + d0 + 4 * q4) =
           f32x4{o[4 * q4], o[4 * q4 + 1], o[4 * q4 + 2], o[4 * q4 + 3]};
+    return;
   }
+  // In-launch merge: store the partial with device-scope stores, wait for
+  // them to complete, then take a ticket; the split that takes the last one
+  // finds every other split's partial complete in memory and merges them.
+  __shared__ uint32_t sm_ticket;
+  const __amdgpu_buffer_rsrc_t pb = dev_buffer(ib, (uint32_t)(a.nsplit * pf * 4));
+  if (wave == 0) {
+    if (writer) {
+      const int pb0 = split * (int)pf;
+      if (g4 == 0) {
+        st_dev(pb, 4 * (pb0 + h), m_run);
+        st_dev(pb, 4 * (pb0 + 8 + h), l_run);
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < CW; ++q4)
+        st_dev4(pb, 4 * (pb0 + 16 + h * D + d0 + 4 * q4),
+                f32x4{o[4 * q4], o[4 * q4 + 1], o[4 * q4 + 2], o[4 * q4 + 3]});
+    }
+    wait_stores();
+    if (lane == 0)
+      sm_ticket = __hip_atomic_fetch_add(a.tickets + item, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (sm_ticket != (uint32_t)(a.nsplit - 1)) return;
+  asm volatile("" ::: "memory");  // the partial loads stay behind the ticket
+  merge_partials<D, NW * 64>(pb, a, vec_off(0), KIND == kEncoderFused ? (int64_t)a.Hkv * D : D,
+                             (int)threadIdx.x);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.tickets + item, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Merge the split partials of one item: out = sum_j 2^(m_j - M) num_j / sum_j 2^(m_j - M) l_j.
@@ -849,7 +949,7 @@ hipError_t launch_kind(const AttnArgs& args, int items, hipStream_t stream) {
     e = launch_nw<D, 2, KIND, COMP, SF>(args, items, stream);
   else
     e = launch_nw<D, 4, KIND, COMP, SF>(args, items, stream);
-  if (e != hipSuccess || args.nsplit == 1) return e;
+  if (e != hipSuccess || args.nsplit == 1 || args.tickets) return e;
   hipLaunchKernelGGL((combine_kernel<D, KIND>), dim3(items), dim3(kCombineThreads), 0, stream,
                      args);
   return hipGetLastError();

@@ -233,6 +233,39 @@ __device__ __forceinline__ u32x2 ld8_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
+// Device-scope accesses for data that one workgroup hands to another within a
+// launch.  The eight XCDs' L2 caches are not coherent with each other, and an
+// agent-scope release/acquire makes them so by writing back and invalidating
+// the whole L2 -- in the middle of a launch that streams the cache through it.
+// Instead only the handed-over words use the device-scope cache policy (sc1):
+// such a store writes through to memory, such a load is not served from a
+// possibly stale L1 or L2 copy (the accesses an agent-scope relaxed atomic
+// load or store compiles to).  Order comes from waiting for the stores to
+// complete (wait_stores) before the hand-over's atomic counter.
+constexpr int kDeviceScope = 16;  // buffer cache-policy operand: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_buffer(const void* p, uint32_t bytes) {
+  // word 3: the gfx9 family's raw-buffer format (32-bit data, untyped access)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ void st_dev(__amdgpu_buffer_rsrc_t r, int byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, kDeviceScope);
+}
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, int byte_off, const f32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0,
+                                         kDeviceScope);
+}
+__device__ __forceinline__ float ld_dev(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kDeviceScope));
+}
+__device__ __forceinline__ f32x4 ld_dev4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kDeviceScope));
+}
+// Wait until every store this wave issued has completed (and keep the
+// compiler from moving memory accesses across the wait).
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Address of row r of (layer, stream, head) in a cache tensor.
 struct KvAddr {
   int64_t ls, ss, hs, rs;

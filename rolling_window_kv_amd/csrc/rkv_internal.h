@@ -25,6 +25,10 @@ struct AttnArgs {
   const uint16_t* vnew;
   void* out;
   float* ws;          // split partials (nsplit > 1)
+  // One counter per item (nsplit > 1): the split that takes the last ticket
+  // merges the item's partials in this launch and returns the counter to 0.
+  // Null: the partials are merged by a second launch (combine_kernel).
+  uint32_t* tickets;
   int32_t S, L, Hkv;  // streams, layers, KV heads (ENC: heads)
   int32_t G;          // query vectors per KV head (decoder: Hq/Hkv; ENC: F)
   int32_t F;          // frames per chunk (ENC), 1 otherwise
@@ -43,6 +47,9 @@ enum AttnKind { kDecodeRead = 0, kDecodeFused = 1, kEncoderFused = 2 };
 
 // Number of key-range splits for an attention call.
 int choose_splits(const rkv_cfg* cfg, int32_t slots);
+// Split launches of at most this many workgroups merge their splits in the
+// same launch: one round of resident 4-wave workgroups on 256 CUs (3 per CU).
+constexpr int64_t kMergeInLaunchMaxBlocks = 768;
 // Floats of workspace per (item, split) partial.
 __host__ __device__ inline int64_t partial_floats(int d) { return 16 + 8 * (int64_t)d; }
 

@@ -30,10 +30,12 @@ RKV_MODE_ENC_CHUNK = 2
 RKV_F_COMPENSATED = 1
 RKV_F_OUT_F32 = 2
 RKV_F_KV_FP16 = 4
+RKV_F_MERGE_LAUNCH = 8
 
 RKV_MAX_NEW_ROWS = 8
 RKV_MAX_HEAD_DIM = 128
 RKV_NOALLOC_SCRATCH_BYTES = 16 << 20
+RKV_NOALLOC_MAX_SPLIT_ITEMS = 16384
 
 # Entry points declared in include/rkv.h (checked by the ABI tests).
 ENTRY_POINTS = (
@@ -574,7 +576,8 @@ class Cache:
         # second plan buffer for rkv_decode_step_pipelined (plans alternate)
         self.plan_next = torch.zeros_like(self.plan)
         nbytes = rkv_workspace_bytes(cfg, slots)
-        self.workspace = (torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=device)
+        # zero-filled: the merge counters at its start must be zero at the first call
+        self.workspace = (torch.zeros((nbytes + 3) // 4, dtype=torch.float32, device=device)
                           if nbytes else None)
 
     def plan_host(self) -> np.ndarray:

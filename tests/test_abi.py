@@ -77,7 +77,7 @@ def test_cfg_validation(rkv):
         (dict(num_q_heads=32, num_kv_heads=2), rkv.RKV_EUNSUPPORTED),
         (dict(rebase_chunk=0), rkv.RKV_EINVAL),
         (dict(mode=7), rkv.RKV_EUNSUPPORTED),
-        (dict(flags=8), rkv.RKV_EUNSUPPORTED),
+        (dict(flags=16), rkv.RKV_EUNSUPPORTED),
         (dict(rope_base=-1.0), rkv.RKV_EINVAL),
         (dict(rope_base=float("inf")), rkv.RKV_EINVAL),
         (dict(softmax_scale=-1.0), rkv.RKV_EINVAL),
@@ -177,24 +177,35 @@ def test_capacity_beyond_the_ring_is_rejected(rkv):
 
 
 def test_workspace_sizes(rkv):
+    # a split call's workspace: one uint32 merge counter per (layer, stream,
+    # kv head) item padded to 256 bytes, then the float32 partials
+    part = (16 + 8 * 128) * 4
     # 36 x 64 x 2 = 4608 items: no split needed
     assert rkv.rkv_workspace_bytes(good_cfg(rkv, num_streams=64, num_layers=36), 375) == 0
     # one stream, one layer, W = 375: splits of 256 keys at least, so none
     one = dict(num_streams=1, num_layers=1)
     assert rkv.rkv_workspace_bytes(good_cfg(rkv, **one), 375) == 0
     # ... with 2048 keys: 8 ranges (2 items, 2048 / 256 keys each)
-    assert rkv.rkv_workspace_bytes(good_cfg(rkv, **one), 2048) == 2 * 8 * (16 + 8 * 128) * 4
+    assert rkv.rkv_workspace_bytes(good_cfg(rkv, **one), 2048) == 256 + 2 * 8 * part
     # re-base every position with the residual: splits of about 48 keys,
     # round(375 / 48) = 8, round(250 / 48) = 5
     comp = good_cfg(rkv, rebase_chunk=1, flags=rkv.RKV_F_COMPENSATED, **one)
-    assert rkv.rkv_workspace_bytes(comp, 375) == 2 * 8 * (16 + 8 * 128) * 4
-    assert rkv.rkv_workspace_bytes(comp, 250) == 2 * 5 * (16 + 8 * 128) * 4
+    assert rkv.rkv_workspace_bytes(comp, 375) == 256 + 2 * 8 * part
+    assert rkv.rkv_workspace_bytes(comp, 250) == 256 + 2 * 5 * part
     # an explicit count is kept up to one split per 16 slots and 64 in all
     assert rkv.rkv_workspace_bytes(good_cfg(rkv, num_splits=6, **one), 375) == \
-        2 * 6 * (16 + 8 * 128) * 4
+        256 + 2 * 6 * part
     assert rkv.rkv_workspace_bytes(good_cfg(rkv, num_splits=100, **one), 8192) == \
-        2 * 64 * (16 + 8 * 128) * 4
+        256 + 2 * 64 * part
+    # the separate merge launch keeps the same layout
+    sep = good_cfg(rkv, num_splits=6, flags=rkv.RKV_F_MERGE_LAUNCH, **one)
+    assert rkv.rkv_workspace_bytes(sep, 375) == 256 + 2 * 6 * part
+    # 130 items: the counters take 520 bytes, padded to 768
+    many = good_cfg(rkv, num_streams=65, num_layers=1, num_splits=2)
+    assert rkv.rkv_workspace_bytes(many, 375) == 768 + 130 * 2 * part
     assert rkv.rkv_workspace_bytes(good_cfg(rkv, head_dim=3), 375) == 0
+    assert rkv.rkv_validate_cfg(good_cfg(rkv, flags=rkv.RKV_F_MERGE_LAUNCH)) == rkv.RKV_OK
+    assert rkv.rkv_validate_cfg(good_cfg(rkv, flags=16)) == rkv.RKV_EUNSUPPORTED
 
 
 FAKE = 0x10000           # never dereferenced: every call below fails validation
@@ -329,7 +340,7 @@ def test_fp16_cache_flag(rkv):
     enc = rkv.make_cfg(2, 1, num_q_heads=4, num_kv_heads=4, head_dim=64,
                        mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=4, flags=rkv.RKV_F_KV_FP16)
     assert rkv.lib().rkv_validate_cfg(ctypes.byref(enc)) == rkv.RKV_EUNSUPPORTED
-    unknown = good_cfg(rkv, flags=1 << 3)
+    unknown = good_cfg(rkv, flags=1 << 4)
     assert rkv.lib().rkv_validate_cfg(ctypes.byref(unknown)) == rkv.RKV_EUNSUPPORTED
 
 
@@ -432,10 +443,10 @@ def test_no_alloc_step_rejects_what_its_array_cannot_hold(rkv):
     assert f(c, F, k, F, N, F, F, N) == rkv.RKV_EINVAL
     assert f(N, F, k, F, F, F, F, N) == rkv.RKV_EINVAL
     # one layer of 64 streams (128 items), 23 splits of a 375-slot ring: 12.2 MB
-    # of partials (128 x 23 x 4,160 bytes) fit ...
+    # of partials (128 x 23 x 4,160 bytes) fit beside the array's merge counters ...
     fits = good_cfg(rkv, num_streams=64, num_layers=1, num_splits=23)
-    assert rkv.rkv_workspace_bytes(fits, 375) == 128 * 23 * 4160
-    assert rkv.rkv_workspace_bytes(fits, 375) < rkv.RKV_NOALLOC_SCRATCH_BYTES
+    assert rkv.rkv_workspace_bytes(fits, 375) == 512 + 128 * 23 * 4160
+    assert 128 * 23 * 4160 < rkv.RKV_NOALLOC_SCRATCH_BYTES - 4 * rkv.RKV_NOALLOC_MAX_SPLIT_ITEMS
     # ... 64 splits of an 8192-slot ring (34 MB) do not
     big = good_cfg(rkv, num_streams=64, num_layers=1, num_splits=64, max_cap=8192)
     big_kv = fake_view(rkv, slots=8192)

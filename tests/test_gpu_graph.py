@@ -31,7 +31,7 @@ def test_per_layer_step_graph_replays_match_eager_calls():
     def setup():
         cache = rkv.Cache(cfg, W, W, W, origins, device=dev)
         views = [rkv.kv_view(cache.k[l:l + 1], cache.v[l:l + 1]) for l in range(L)]
-        ws = torch.empty((nb + 3) // 4, dtype=torch.float32, device=dev)
+        ws = torch.zeros((nb + 3) // 4, dtype=torch.float32, device=dev)
         out = torch.zeros((L, S, 16, 128), dtype=torch.bfloat16, device=dev)
         return cache, views, ws, out
 
