@@ -13,14 +13,21 @@
 // output feature, contiguous in k) is the A operand and the activations (row
 // = token) the B operand, so a lane's result holds four consecutive output
 // features of one token and the epilogue writes them as one vector.  A
-// workgroup computes 64 tokens x 64 features: both operand tiles of a
-// k-stage are staged through LDS (double-buffered; the global loads of the
-// next kDepth stages are in flight during a stage's MFMAs), and each of the 4
-// waves computes a 32 x 32 quarter from them, so every loaded element feeds
-// 64 products instead of 16.  Two workgroups share a CU (two waves per
-// SIMD): a 64 x 128 tile (one workgroup per CU at 512 tokens, 0.75 instead of
-// one operand read per product) measured slower, its single wave per SIMD
-// left with nothing to run while it waits for LDS.
+// workgroup computes 64 tokens x 64 features; each of its 4 waves a 32 x 32
+// quarter, so every element read from LDS feeds 64 products instead of 16.
+// With 512 tokens the products are short in M, and what bounds them is
+// moving operands into and out of LDS, not the matrix cores: with both
+// switched off, the q/k/v launch's loop of LDS writes, reads and barriers
+// alone took 11.2 of its 13.1 us.  So the operand tiles go from global memory
+// straight into LDS (gfx950's global_load_lds_dwordx4: no staging registers
+// and no LDS write instructions) through a ring of NS k-stages, NS - 1 of them
+// in flight.  With the weights cache-resident this takes q/k/v from 13.1 to
+// 9.9 us and the up-projection from 16.2 to 12.3 us (same bits); in the
+// encoder step each layer's weights come cold from HBM once, and there the
+// first touch of the weight panels bounds the products (q/k/v 14.6 -> 14.3
+// us).  Larger tiles (64 x 128, 128 x 64 per workgroup), weights loaded
+// straight into the MFMA operand registers, and a block order that keeps a
+// weight panel's token tiles on one XCD were slower.
 
 #include <math.h>
 
@@ -51,77 +58,83 @@ constexpr int kTM = 64, kTN = 64, kKS = 64;
 // LDS tiles: rows of kKS elements (128 bytes) without padding; the eight
 // 16-byte chunks of row r are stored in the order chunk ^ ((r >> 1) & 7).
 // A 16-lane group of a 16-byte operand read takes one chunk of 16
-// consecutive rows and a group of a staging write two whole rows: either
-// way the swizzle puts the 16 pieces on 16 distinct 4-bank groups of the 64
-// banks.  (Rows padded to 144 bytes left the staging writes 2-way conflicted:
-// the bank-conflict counter read as many cycles as LDS instructions were
-// active.)
+// consecutive rows, which the swizzle puts on 16 distinct 4-bank groups of
+// the 64 banks (rows padded to 144 bytes instead left the stores 2-way
+// conflicted).
 __device__ __forceinline__ int lds_at(int row, int chunk) {
   return row * kKS + 8 * (chunk ^ ((row >> 1) & 7));
 }
-constexpr int kDepth = 2;          // k-stages whose global loads are in flight
+// 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4):
+// lane i of the wave writes l + 16 i bytes, l being the same for every lane.
+__device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+// Wait until at most N of this wave's vector memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 constexpr int kWF = kTN / 2;       // features per wave (2 x 2 waves: 32 tokens x 32 features)
 constexpr int kFB = kWF / 16;      // 16-feature MFMA blocks per wave
-constexpr int kWRows = kTN / 32;   // weight rows each thread stages per k-stage
 
-template <int EP>
+template <int EP, int NS>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmSet set, int M, int N, int K, int ld) {
-  __shared__ __attribute__((aligned(16))) uint16_t sw[2][kTN * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTM * kKS];
+  static_assert(NS >= 2 && NS <= 3, "ring depth");
+  // one k-stage: weight tile [64][kKS], then token tile [64][kKS]; a ring of
+  // NS stages in separate arrays, so the compiler sees that a stage's reads
+  // do not touch the stages still being loaded
+  __shared__ __attribute__((aligned(16))) uint16_t st0[2 * 64 * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[2 * 64 * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[NS > 2 ? 2 * 64 * kKS : 8];
+  auto stage = [&](int slot) -> uint16_t* { return slot == 0 ? st0 : slot == 1 ? st1 : st2; };
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;          // token half, feature half
-  const uint16_t* __restrict__ w = set.w[blockIdx.z];
-  const uint16_t* __restrict__ x = set.x[blockIdx.z];
+  const int bz = blockIdx.z;
+  const uint16_t* __restrict__ w = set.w[bz];
+  const uint16_t* __restrict__ x = set.x[bz];
   const int n0 = blockIdx.x * kTN, m0 = blockIdx.y * kTM;
-  // staging: thread t moves the 16-byte pieces (row t/8 + 32 r, k 8 (t%8)) of
-  // both tiles; token rows past M and feature rows past N (N is a multiple of
-  // 64, so a last tile may hold 64 features) are clamped: read, never stored
-  const int lr = t >> 3, lk = 8 * (t & 7);
-  const uint16_t* wp[kWRows];
+  // Loads: wave v moves rows [16 v, 16 v + 16) of both tiles, 8 rows (1 KB)
+  // per instruction; lane i takes row r0 + i / 8 and lands in its chunk slot
+  // i % 8, which holds logical chunk (i % 8) ^ ((row >> 1) & 7).  Token rows
+  // past M and feature rows past N (N is a multiple of 64, so a last tile may
+  // hold 64 features) are clamped: read, never stored.
+  const uint16_t* src[2][2];
 #pragma unroll
-  for (int r = 0; r < kWRows; ++r) wp[r] = w + (int64_t)min(n0 + 32 * r + lr, N - 1) * ld + lk;
-  const uint16_t* xp0 = x + (int64_t)min(m0 + lr, M - 1) * ld + lk;
-  const uint16_t* xp1 = x + (int64_t)min(m0 + 32 + lr, M - 1) * ld + lk;
+  for (int h = 0; h < 2; ++h) {
+    const int row = 16 * wave + 8 * h + (lane >> 3);
+    const int q = (lane & 7) ^ ((row >> 1) & 7);
+    src[0][h] = w + (int64_t)min(n0 + row, N - 1) * ld + 8 * q;
+    src[1][h] = x + (int64_t)min(m0 + row, M - 1) * ld + 8 * q;
+  }
   const int steps = K / kKS;
-  // register ring: stage s's pieces sit in slot s % kDepth from its load until
-  // its LDS store, which frees the slot for stage s + kDepth
-  u32x4 rw[kDepth][kWRows], rx0[kDepth], rx1[kDepth];
-  auto gload = [&](int s, int slot) {
+  auto issue = [&](int s, int slot) __attribute__((always_inline)) {
     const int k0 = (s < steps ? s : steps - 1) * kKS;   // past the end: a harmless reload
 #pragma unroll
-    for (int r = 0; r < kWRows; ++r) rw[slot][r] = ld16(wp[r] + k0);
-    rx0[slot] = ld16(xp0 + k0);
-    rx1[slot] = ld16(xp1 + k0);
-  };
-  auto lstore = [&](int b, int slot) {
-    const int ch = lk >> 3;
+    for (int o = 0; o < 2; ++o)
 #pragma unroll
-    for (int r = 0; r < kWRows; ++r)
-      *reinterpret_cast<u32x4*>(&sw[b][lds_at(32 * r + lr, ch)]) = rw[slot][r];
-    *reinterpret_cast<u32x4*>(&sx[b][lds_at(lr, ch)]) = rx0[slot];
-    *reinterpret_cast<u32x4*>(&sx[b][lds_at(32 + lr, ch)]) = rx1[slot];
+      for (int h = 0; h < 2; ++h)
+        lds_dma16(src[o][h] + k0, stage(slot) + (o * 64 + 16 * wave + 8 * h) * kKS);
   };
   f32x4 acc[2][kFB];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < kFB; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // operand fragments of one 32-k chunk: the next chunk's are read from LDS
-  // before this chunk's products are issued, so the LDS latency hides behind
-  // them (read and used at once, the wave waits for every read)
-  auto frag = [&](int b, int kk, bf16x8* fa, bf16x8* fb) __attribute__((always_inline)) {
+  auto frag = [&](int slot, int kk, bf16x8* fa, bf16x8* fb) __attribute__((always_inline)) {
+    const uint16_t* b = stage(slot);
 #pragma unroll
     for (int i = 0; i < kFB; ++i)
       fa[i] = __builtin_bit_cast(
-          bf16x8,
-          *reinterpret_cast<const u32x4*>(&sw[b][lds_at(wn * kWF + 16 * i + c, (kk >> 3) + g)]));
+          bf16x8, *reinterpret_cast<const u32x4*>(&b[lds_at(wn * kWF + 16 * i + c, (kk >> 3) + g)]));
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       fb[j] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(&sx[b][lds_at(wm * 32 + 16 * j + c, (kk >> 3) + g)]));
+          bf16x8,
+          *reinterpret_cast<const u32x4*>(&b[lds_at(64 + wm * 32 + 16 * j + c, (kk >> 3) + g)]));
   };
   auto mma = [&](const bf16x8* fa, const bf16x8* fb) __attribute__((always_inline)) {
 #pragma unroll
@@ -131,31 +144,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmSet set, int M, int N, in
         acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[j][i], 0, 0, 0);
   };
   static_assert(kKS == 64, "a k-stage is two 32-k chunks");
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s, s);
   bf16x8 fa0[kFB], fb0[2], fa1[kFB], fb1[2];
+  for (int s0 = 0; s0 < steps; s0 += NS) {
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) gload(d, d);
-  lstore(0, 0);
-  gload(kDepth, 0);
-  __syncthreads();
-  frag(0, 0, fa0, fb0);
-  for (int s0 = 0; s0 < steps; s0 += kDepth) {
-#pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
+    for (int u = 0; u < NS; ++u) {
       const int s = s0 + u;
       if (s < steps) {
-        const int b = u & 1;                            // kDepth even: s & 1
-        frag(b, 32, fa1, fb1);
+        // this wave's 4 loads of stage s are in LDS (those of the NS - 2
+        // later stages may still be in flight) ...
+        wait_loads<4 * (NS - 2)>();
+        // ... and every wave's are; every wave has also finished reading
+        // stage s - 1, whose slot is loaded next
+        __builtin_amdgcn_s_barrier();
+        issue(s + NS - 1, (u + NS - 1) % NS);
+        frag(u, 0, fa0, fb0);
+        frag(u, 32, fa1, fb1);
         mma(fa0, fb0);
-        // the LDS buffer written here was last read in stage s - 1, which every
-        // wave finished before the barrier that ended it
-        if (s + 1 < steps) {
-          const int slot = (u + 1) % kDepth;
-          lstore(b ^ 1, slot);
-          if (s + 1 + kDepth < steps) gload(s + 1 + kDepth, slot);
-        }
         mma(fa1, fb1);
-        __syncthreads();
-        if (s + 1 < steps) frag(b ^ 1, 0, fa0, fb0);
       }
     }
   }
@@ -171,11 +178,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmSet set, int M, int N, in
       const int n = n0 + kWF * wn + 16 * i + 4 * g;
       if (n >= N) continue;
       if (EP == kAddF32) {
-        float* p = reinterpret_cast<float*>(set.c[blockIdx.z]) + (int64_t)m * N + n;
+        float* p = reinterpret_cast<float*>(set.c[bz]) + (int64_t)m * N + n;
         const f32x4 old = *reinterpret_cast<const f32x4*>(p);
         *reinterpret_cast<f32x4*>(p) = old + v;
       } else if (EP == kStoreF32) {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(set.c[blockIdx.z]) + (int64_t)m * N +
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(set.c[bz]) + (int64_t)m * N +
                                   n) = v;
       } else {
         float e0 = v[0], e1 = v[1], e2 = v[2], e3 = v[3];
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmSet set, int M, int N, in
           e2 = gelu_erf(e2);
           e3 = gelu_erf(e3);
         }
-        uint16_t* p = reinterpret_cast<uint16_t*>(set.c[blockIdx.z]) + (int64_t)m * N + n;
+        uint16_t* p = reinterpret_cast<uint16_t*>(set.c[bz]) + (int64_t)m * N + n;
         *reinterpret_cast<u32x2*>(p) = u32x2{cvt2_bf16(e0, e1), cvt2_bf16(e2, e3)};
       }
     }
@@ -290,18 +297,35 @@ hipError_t launch_gemm(GemmEpilogue ep, const uint16_t* const* w, const uint16_t
     set.c[i] = c[i];
   }
   const dim3 grid((N + kTN - 1) / kTN, (M + kTM - 1) / kTM, count);
+  // Three k-stages in the ring (two in flight), or two for short products
+  // (fewer than 10 k-stages), whose prologue the deeper ring does not repay.
+  // Measured at 512 tokens with each product's weights read cold from HBM,
+  // as in the encoder step, old kernel -> two -> three stages: q/k/v 14.6 ->
+  // 17.3 -> 14.3 us, up-projection 18.8 -> 19.7 -> 18.2, down-projection
+  // 18.4 -> 19.4 -> 18.4, output projection (k-slices of 320) 7.8 -> 7.0 ->
+  // 7.4; with the weights cache-resident q/k/v takes 13.0 -> 11.2 -> 9.9 us.
+  const bool deep = K / kKS >= 10;
   switch (ep) {
     case GemmEpilogue::kStoreBf16:
-      hipLaunchKernelGGL((gemm_kernel<kStoreBf16>), grid, dim3(256), 0, stream, set, M, N, K, ld);
+      if (deep)
+        hipLaunchKernelGGL((gemm_kernel<kStoreBf16, 3>), grid, dim3(256), 0, stream, set, M, N, K, ld);
+      else
+        hipLaunchKernelGGL((gemm_kernel<kStoreBf16, 2>), grid, dim3(256), 0, stream, set, M, N, K, ld);
       break;
     case GemmEpilogue::kAddF32:
-      hipLaunchKernelGGL((gemm_kernel<kAddF32>), grid, dim3(256), 0, stream, set, M, N, K, ld);
+      hipLaunchKernelGGL((gemm_kernel<kAddF32, 2>), grid, dim3(256), 0, stream, set, M, N, K, ld);
       break;
     case GemmEpilogue::kGeluBf16:
-      hipLaunchKernelGGL((gemm_kernel<kGeluBf16>), grid, dim3(256), 0, stream, set, M, N, K, ld);
+      if (deep)
+        hipLaunchKernelGGL((gemm_kernel<kGeluBf16, 3>), grid, dim3(256), 0, stream, set, M, N, K, ld);
+      else
+        hipLaunchKernelGGL((gemm_kernel<kGeluBf16, 2>), grid, dim3(256), 0, stream, set, M, N, K, ld);
       break;
     default:
-      hipLaunchKernelGGL((gemm_kernel<kStoreF32>), grid, dim3(256), 0, stream, set, M, N, K, ld);
+      if (deep)
+        hipLaunchKernelGGL((gemm_kernel<kStoreF32, 3>), grid, dim3(256), 0, stream, set, M, N, K, ld);
+      else
+        hipLaunchKernelGGL((gemm_kernel<kStoreF32, 2>), grid, dim3(256), 0, stream, set, M, N, K, ld);
       break;
   }
   return hipGetLastError();
