@@ -149,6 +149,10 @@ int scratch_address(void** out) {
   return RKV_OK;
 }
 
+// Workgroups that pull an encoder step's next weights into the cache during
+// a chunk-attention launch (one per CU).
+constexpr int kPullBlocks = 256;
+
 // ws == kUseScratch: the split partials go to the library's scratch array
 // (after every argument check, so errors still come before any HIP call).
 void* const kUseScratch = reinterpret_cast<void*>(~(uintptr_t)0);
@@ -156,7 +160,8 @@ void* const kUseScratch = reinterpret_cast<void*>(~(uintptr_t)0);
 int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
               const rkv_kv_view* kv, const void* q, const void* knew, const void* vnew,
               void* out, void* ws, size_t ws_bytes, void* stream,
-              rkv_stream_state* next_state = nullptr, rkv_step_plan* next_plan = nullptr) {
+              rkv_stream_state* next_state = nullptr, rkv_step_plan* next_plan = nullptr,
+              const void* pull = nullptr, size_t pull_bytes = 0) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (next_state || next_plan) {
@@ -230,6 +235,10 @@ int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
   a.adv_F = cfg->new_rows;
   a.adv_half = cfg->head_dim / 2;
   a.adv_theta = rkv::theta_table(cfg);
+  const bool pulls = kind == rkv::kEncoderFused && pull && pull_bytes >= 16;
+  a.pull = pulls ? static_cast<const char*>(pull) : nullptr;
+  a.pull_bytes = pulls ? (int64_t)(pull_bytes & ~(size_t)15) : 0;
+  a.pull_blocks = pulls ? kPullBlocks : 0;
   return hip_status(rkv::launch_attention(cfg, kind, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -605,8 +614,15 @@ int rkv_encoder_step(const rkv_cfg* cfg, const rkv_encoder_cfg* ec, const rkv_st
     rkv_kv_view lv = *kv;
     lv.k = static_cast<uint16_t*>(kv->k) + (size_t)l * kv->layer_stride;
     lv.v = static_cast<uint16_t*>(kv->v) + (size_t)l * kv->layer_stride;
+    // While the attention streams this layer's window, its extra workgroups
+    // pull the weights of the next four products into the infinity cache:
+    // Wo, g2, W1, W2 of this layer and g1, Wq, Wk, Wv of the next, which lie
+    // back to back (a product reading its weights cold from HBM is limited by
+    // the first touch of each weight panel: q/k/v 14.1 against 11.6 us).
+    const size_t pull_elems = (size_t)H * H + H + 2 * (size_t)FF * H +
+                              (l + 1 < cfg->num_layers ? H + 3 * (size_t)H * H : 0);
     if ((rc = attention(&one, rkv::kEncoderFused, d_plan, &lv, q, k, v, att, aws, aws_bytes,
-                        hip_stream)))
+                        hip_stream, nullptr, nullptr, wo, 2 * pull_elems)))
       return rc;
     // output projection in `so` k-slices; x += their sum, a = RMSNorm(x) g2
     const uint16_t* ws_[rkv::kGemmMaxSet];

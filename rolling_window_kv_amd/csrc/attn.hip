@@ -250,12 +250,25 @@ void attn_kernel(AttnArgs args) {
   a.adv_dc = args.adv_dc;
   a.adv_F = args.adv_F;
   a.adv_half = args.adv_half;
+  a.pull = args.pull;
+  a.pull_bytes = args.pull_bytes;
+  a.pull_blocks = args.pull_blocks;
   asm volatile("" : : "s"(a.plan), "s"(a.ring.k), "s"(a.ring.v), "s"(a.ring.klo), "s"(a.ring.ls),
                "s"(a.ring.ss), "s"(a.ring.hs), "s"(a.ring.rs), "s"(a.ring.slots));
   asm volatile("" : : "s"(a.q), "s"(a.knew), "s"(a.vnew), "s"(a.out), "s"(a.ws), "s"(a.S),
                "s"(a.L), "s"(a.Hkv), "s"(a.G), "s"(a.F), "s"(a.nsplit), "s"(a.out_f32),
                "s"(a.scale_log2), "s"(a.adv_state), "s"(a.tickets));
 
+  // Encoder step: the blocks past the attention grid pull the next products'
+  // weights into the cache while the attention drains.
+  if (KIND == kEncoderFused && a.pull) {
+    const int njobs = a.L * a.S * a.Hkv * a.nsplit;
+    if ((int)blockIdx.x >= njobs) {
+      pull_into_cache(a.pull, a.pull_bytes, (int)blockIdx.x - njobs, a.pull_blocks,
+                      reinterpret_cast<uint16_t*>(&sm_q[0][0]));
+      return;
+    }
+  }
   // Pipelined decode step: the blocks past the attention grid compute the
   // next step's plan, one wave per stream (nothing in this launch reads it).
   if ((KIND == kDecodeFused || KIND == kDecodeRead) && a.adv_state) {
@@ -936,7 +949,8 @@ constexpr int64_t kManyItems = 12288;
 
 template <int D, int NW, int KIND, bool COMP, typename SF>
 hipError_t launch_nw(const AttnArgs& args, int items, hipStream_t stream) {
-  const int extra = args.adv_state ? (args.S + NW - 1) / NW : 0;
+  const int extra = args.adv_state ? (args.S + NW - 1) / NW
+                                    : (KIND == kEncoderFused && args.pull ? args.pull_blocks : 0);
   hipLaunchKernelGGL((attn_kernel<D, NW, KIND, COMP, SF>),
                      dim3(items * args.nsplit + extra), dim3(NW * 64), 0, stream, args);
   return hipGetLastError();

@@ -64,11 +64,6 @@ constexpr int kTM = 64, kTN = 64, kKS = 64;
 __device__ __forceinline__ int lds_at(int row, int chunk) {
   return row * kKS + 8 * (chunk ^ ((row >> 1) & 7));
 }
-// 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4):
-// lane i of the wave writes l + 16 i bytes, l being the same for every lane.
-__device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
-}
 // Wait until at most N of this wave's vector memory loads are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_loads() {

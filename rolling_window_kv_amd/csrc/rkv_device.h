@@ -266,6 +266,28 @@ __device__ __forceinline__ f32x4 ld_dev4(__amdgpu_buffer_rsrc_t r, int byte_off)
 // compiler from moving memory accesses across the wait).
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4):
+// lane i of the wave writes l + 16 i bytes, l being the same for every lane.
+__device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
+// Reads [p, p + bytes) once, 1 KB per wave instruction, into one scratch KB of
+// LDS (every wave overwrites the same bytes), so that the lines are in the
+// infinity cache when a later launch reads them; workgroup wg of nwg.  The
+// data goes nowhere else; a wave's end waits for its loads.
+__device__ __forceinline__ void pull_into_cache(const char* p, int64_t bytes, int wg, int nwg,
+                                                uint16_t* lds_scratch_1kb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int64_t last = bytes - 16;
+  for (int64_t off = ((int64_t)wg * nw + wave) * 1024; off < bytes;
+       off += (int64_t)nwg * nw * 1024) {
+    int64_t o = off + 16 * lane;
+    o = o < last ? o : last;
+    lds_dma16(reinterpret_cast<const uint16_t*>(p + o), lds_scratch_1kb);
+  }
+}
+
 // Address of row r of (layer, stream, head) in a cache tensor.
 struct KvAddr {
   int64_t ls, ss, hs, rs;

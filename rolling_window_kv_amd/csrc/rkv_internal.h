@@ -40,6 +40,12 @@ struct AttnArgs {
   rkv_stream_state* adv_state;
   rkv_step_plan* adv_plan;
   int32_t adv_mode, adv_dc, adv_F, adv_half;
+  // Encoder chunks: pull_blocks extra workgroups, dispatched after the
+  // attention's, read [pull, pull + pull_bytes) into the cache (the next
+  // products' weights of an encoder step); null: none.
+  const char* pull;
+  int64_t pull_bytes;
+  int32_t pull_blocks;
   Theta adv_theta;
 };
 
