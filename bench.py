@@ -381,6 +381,10 @@ def run_gpu(c, args):
                               A.to(dev), mod, sp)
         cond = torch.arange(S, dtype=torch.int32, device=dev) % len(conds)
         tcond = (tc, mod, cond)
+    # the pipelined step applies the conditioning as it stores its output
+    # (--tcond-pass: a separate rkv_tcond_modulate launch after the step)
+    tcond_fused = tcond is not None and pipelined and args.path == "pipelined" and \
+        not args.tcond_pass
 
     def step(i, ev=None):
         j = i % P
@@ -402,12 +406,16 @@ def run_gpu(c, args):
                 rkv.rkv_update_step(cfg, cur, cache.kv, k[j], v[j], sp)
                 rkv.rkv_decode_attn_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[j], out,
                                               ws, sp)
+            elif tcond_fused:
+                rkv.rkv_decode_step_pipelined_tcond(cfg, tcond[0], tcond[1], tcond[2],
+                                                    cache.state, cur, nxt, cache.kv, q[j], k[j],
+                                                    v[j], out, ws, sp)
             else:
                 rkv.rkv_decode_step_pipelined(cfg, cache.state, cur, nxt, cache.kv, q[j], k[j],
                                               v[j], out, ws, sp)
             if ev is not None:
                 ev[1].record(stream)
-            if tcond is not None:
+            if tcond is not None and not tcond_fused:
                 rkv.rkv_tcond_modulate(cfg, tcond[0], tcond[1], tcond[2], out, sp)
             return
         rkv.rkv_advance(cfg, cache.state, cache.plan, sp)
@@ -480,7 +488,7 @@ def run_gpu(c, args):
     K = args.steps
     RUN = 8
     bracket = (pipelined and args.path == "pipelined" and c["mode"] == "rebase"
-               and tcond is None)
+               and (tcond is None or tcond_fused))
     if per_layer is not None:
         args.kernel_events = False    # the roofline uses the whole step's time
     runs = []                          # (first, last + 1) timed-step ranges
@@ -515,7 +523,8 @@ def run_gpu(c, args):
         kernel_ms = sum(ev[n][0].elapsed_time(ev[n][1]) for n, _ in runs) / kernel_samples
         kernel_bytes = launch_bytes(c, windows, origins, timed) / kernel_samples
     copy_gbps = device_copy_gbps()     # after the timed region
-    return dict(cfg=cfg, elapsed_ms=elapsed_ms, kernel_ms=kernel_ms, kernel_bytes=kernel_bytes,
+    return dict(cfg=cfg, tcond_fused=tcond_fused, elapsed_ms=elapsed_ms, kernel_ms=kernel_ms,
+                kernel_bytes=kernel_bytes,
                 wall_s=wall, kernel_samples=kernel_samples, copy_gbps=copy_gbps,
                 first_timed_step=i0, windows=windows, origins=origins,
                 kernel_timing=("event pairs around runs of %d back-to-back launches, every "
@@ -783,6 +792,7 @@ def bench_config(args):
     args.warmup = c["warmup"] if args.warmup is None else args.warmup
 
     r = run_gpu(c, args)
+    tcond_fused = r["tcond_fused"]
     L, S, K = c["L"], c["S"], args.steps
     secs = r["elapsed_ms"] / 1e3
     sl_steps = L * S * K / secs
@@ -844,7 +854,9 @@ def bench_config(args):
                            else (args.path if c["mode"] != "enc" else "fused"),
                    "alg_bytes_per_stream_layer_step": b_sl,
                    **({"layout": args.layout} if args.layout != "interleaved" else {}),
-                   **({"tcond": "rkv_tcond_modulate after each step, 8 settings, dim 256"}
+                   **({"tcond": ("applied as the attention stores its output "
+                                 "(rkv_decode_step_pipelined_tcond)" if tcond_fused else
+                                 "rkv_tcond_modulate after each step") + ", 8 settings, dim 256"}
                       if args.tcond else {})},
         "achieved_GBps_step": round(step_gbps, 1),
         "device_copy_GBps": round(r["copy_gbps"], 1),
@@ -902,6 +914,9 @@ def main():
     ap.add_argument("--tcond", action="store_true",
                     help="apply the delay conditioning (rkv_tcond_modulate) to every step's "
                          "attention output (decoder workloads)")
+    ap.add_argument("--tcond-pass", action="store_true",
+                    help="with --tcond: modulate in a separate rkv_tcond_modulate launch after "
+                         "each step instead of in the attention launch")
     ap.add_argument("--kv-fp16", action="store_true",
                     help="store K and V as fp16 (the fp16 cache variant; decoder workloads)")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")

@@ -576,6 +576,21 @@ int rkv_tcond_prepare(const rkv_tcond_cfg* tc, const int32_t* h_num_delay,
 int rkv_tcond_modulate(const rkv_cfg* cfg, const rkv_tcond_cfg* tc, const float* d_mod,
                        const int32_t* d_stream_cond, void* d_out, void* hip_stream);
 
+/* The pipelined decode step with the delay conditioning applied as the
+ * attention output is stored (Audio8 explainer, 可配置转写延迟: the condition
+ * enters after each decoder layer's attention): bit-identical to
+ * rkv_decode_step_pipelined followed by rkv_tcond_modulate with the same
+ * d_mod and d_stream_cond, in one launch instead of two.  Arguments as
+ * those two calls; REBASE and COMPACT modes (RKV_EINVAL for ENC_CHUNK), tc
+ * matching cfg as for rkv_tcond_modulate. */
+int rkv_decode_step_pipelined_tcond(const rkv_cfg* cfg, const rkv_tcond_cfg* tc,
+                                    const float* d_mod, const int32_t* d_stream_cond,
+                                    rkv_stream_state* d_state, const rkv_step_plan* d_plan,
+                                    rkv_step_plan* d_plan_next, const rkv_kv_view* kv,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    void* out, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -161,7 +161,9 @@ int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
               const rkv_kv_view* kv, const void* q, const void* knew, const void* vnew,
               void* out, void* ws, size_t ws_bytes, void* stream,
               rkv_stream_state* next_state = nullptr, rkv_step_plan* next_plan = nullptr,
-              const void* pull = nullptr, size_t pull_bytes = 0) {
+              const void* pull = nullptr, size_t pull_bytes = 0,
+              const float* tc_mod = nullptr, const int32_t* tc_cond = nullptr,
+              int32_t tc_conds = 0) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (next_state || next_plan) {
@@ -239,6 +241,10 @@ int attention(const rkv_cfg* cfg, rkv::AttnKind kind, const rkv_step_plan* plan,
   a.pull = pulls ? static_cast<const char*>(pull) : nullptr;
   a.pull_bytes = pulls ? (int64_t)(pull_bytes & ~(size_t)15) : 0;
   a.pull_blocks = pulls ? kPullBlocks : 0;
+  const bool tcond = kind != rkv::kEncoderFused && tc_mod && tc_cond && tc_conds > 0;
+  a.tc_mod = tcond ? tc_mod : nullptr;
+  a.tc_cond = tcond ? tc_cond : nullptr;
+  a.tc_conds = tcond ? tc_conds : 0;
   return hip_status(rkv::launch_attention(cfg, kind, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -734,4 +740,24 @@ int rkv_tcond_modulate(const rkv_cfg* cfg, const rkv_tcond_cfg* tc, const float*
       cfg->num_layers, cfg->num_streams, hidden, tc->num_conds,
       (cfg->flags & RKV_F_OUT_F32) != 0, d_mod, d_stream_cond, d_out,
       static_cast<hipStream_t>(hip_stream)));
+}
+
+int rkv_decode_step_pipelined_tcond(const rkv_cfg* cfg, const rkv_tcond_cfg* tc,
+                                    const float* d_mod, const int32_t* d_stream_cond,
+                                    rkv_stream_state* d_state, const rkv_step_plan* d_plan,
+                                    rkv_step_plan* d_plan_next, const rkv_kv_view* kv,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    void* out, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (cfg->mode == RKV_MODE_ENC_CHUNK) return RKV_EINVAL;
+  if ((rc = check_tcond(tc))) return rc;
+  if (tc->num_layers != cfg->num_layers || tc->hidden != cfg->num_q_heads * cfg->head_dim)
+    return RKV_EINVAL;
+  if (!d_stream_cond) return RKV_EINVAL;
+  if ((rc = check_ptr(d_mod))) return rc;
+  return attention(cfg, rkv::kDecodeFused, d_plan, kv, q, k_new, v_new, out, workspace,
+                   workspace_bytes, hip_stream, d_state, d_plan_next, nullptr, 0, d_mod,
+                   d_stream_cond, tc->num_conds);
 }

@@ -154,7 +154,8 @@ struct Occupancy {
 // `hstride` the distance between heads.
 template <int D, int NT>
 __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t pb, const AttnArgs& a,
-                                               int64_t base, int64_t hstride, int tid) {
+                                               int64_t base, int64_t hstride, int tid,
+                                               const float* tg) {
   const int ns = a.nsplit;
   const int pf = (int)partial_floats(D);
   const int nq = a.G * (D / 4);
@@ -195,6 +196,17 @@ __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t pb, const 
 #pragma unroll
     for (int k = 0; k < 4; ++k) o4[k] = den > 0.f ? num[k] / den : 0.f;
     const int64_t off = base + hh * hstride + dd;
+    // delay conditioning of the stored value (tg: gamma of head 0, beta a
+    // hidden width later; decoder only)
+    if (tg) {
+      const int hidden = a.Hkv * a.G * D;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = hh * D + dd + k;
+        const float x = a.out_f32 ? o4[k] : bf2f(f2bf(o4[k]));
+        o4[k] = fmaf(x, 1.0f + tg[i], tg[hidden + i]);
+      }
+    }
     if (a.out_f32)
       *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) =
           f32x4{o4[0], o4[1], o4[2], o4[3]};
@@ -253,6 +265,9 @@ void attn_kernel(AttnArgs args) {
   a.pull = args.pull;
   a.pull_bytes = args.pull_bytes;
   a.pull_blocks = args.pull_blocks;
+  a.tc_mod = args.tc_mod;
+  a.tc_cond = args.tc_cond;
+  a.tc_conds = args.tc_conds;
   asm volatile("" : : "s"(a.plan), "s"(a.ring.k), "s"(a.ring.v), "s"(a.ring.klo), "s"(a.ring.ls),
                "s"(a.ring.ss), "s"(a.ring.hs), "s"(a.ring.rs), "s"(a.ring.slots));
   asm volatile("" : : "s"(a.q), "s"(a.knew), "s"(a.vnew), "s"(a.out), "s"(a.ws), "s"(a.S),
@@ -308,6 +323,8 @@ void attn_kernel(AttnArgs args) {
   const uint32_t hd3 = *reinterpret_cast<const uint32_t*>(phb +
                                                           offsetof(rkv_step_plan, rebase_delta));
   const u32x2 hd4 = *reinterpret_cast<const u32x2*>(phb + offsetof(rkv_step_plan, cap));
+  // delay conditioning: the stream's condition, requested with the set-up
+  const int tc_c = (KIND != kEncoderFused && a.tc_mod) ? a.tc_cond[s] : -1;
 
   const int slots = a.ring.slots;
   const int per = (((slots + a.nsplit - 1) / a.nsplit) + TK - 1) & ~(TK - 1);
@@ -744,6 +761,21 @@ void attn_kernel(AttnArgs args) {
   };
   if (ntiles > 0) run_tiles(std::integral_constant<bool, true>());
 
+  // Delay conditioning of an unsplit item: the writing lanes request their
+  // gamma and beta now, so the wave merge below hides the loads' latency.
+  const int tc_hidden = a.Hkv * a.G * D;
+  const bool tc_on = KIND != kEncoderFused && a.nsplit == 1 && tc_c >= 0 && tc_c < a.tc_conds;
+  f32x4 tc_g[CW], tc_b[CW];
+  if (tc_on && wave == 0 && c < 8 && c < a.G) {
+    const float* tg = a.tc_mod + ((int64_t)l * a.tc_conds + tc_c) * 2 * tc_hidden +
+                      (g * a.G + c) * D + 4 * CW * g4;
+#pragma unroll
+    for (int q4 = 0; q4 < CW; ++q4) {
+      tc_g[q4] = *reinterpret_cast<const f32x4*>(tg + 4 * q4);
+      tc_b[q4] = *reinterpret_cast<const f32x4*>(tg + tc_hidden + 4 * q4);
+    }
+  }
+
   // ---- per-wave reduction: row sums over lane groups, hi+lo columns ----
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
@@ -803,9 +835,15 @@ void attn_kernel(AttnArgs args) {
     if (a.out_f32) {
       float* op = reinterpret_cast<float*>(a.out) + off;
 #pragma unroll
-      for (int q4 = 0; q4 < CW; ++q4)
-        *reinterpret_cast<f32x4*>(op + 4 * q4) =
+      for (int q4 = 0; q4 < CW; ++q4) {
+        f32x4 v =
             f32x4{o[4 * q4] * inv, o[4 * q4 + 1] * inv, o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv};
+        if (tc_on) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = fmaf(v[k], 1.0f + tc_g[q4][k], tc_b[q4][k]);
+        }
+        *reinterpret_cast<f32x4*>(op + 4 * q4) = v;
+      }
     } else {
       uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + off;
 #pragma unroll
@@ -814,6 +852,18 @@ void attn_kernel(AttnArgs args) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           w[k] = cvt2_bf16(o[8 * q8 + 2 * k] * inv, o[8 * q8 + 2 * k + 1] * inv);
+        if (tc_on) {
+          // modulate the stored (rounded) value, as a separate pass would
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int i = 8 * q8 + 2 * k;   // dims i, i + 1 of the lane's 4 CW
+            const float y0 = fmaf(bf2f(w[k] & 0xffffu), 1.0f + tc_g[i >> 2][i & 3],
+                                  tc_b[i >> 2][i & 3]);
+            const float y1 = fmaf(bf2f(w[k] >> 16), 1.0f + tc_g[(i + 1) >> 2][(i + 1) & 3],
+                                  tc_b[(i + 1) >> 2][(i + 1) & 3]);
+            w[k] = f2bf(y0) | (f2bf(y1) << 16);
+          }
+        }
         st16(op + 8 * q8, w);
       }
     }
@@ -860,8 +910,10 @@ void attn_kernel(AttnArgs args) {
   __syncthreads();
   if (sm_ticket != (uint32_t)(a.nsplit - 1)) return;
   asm volatile("" ::: "memory");  // the partial loads stay behind the ticket
+  const float* tg =
+      KIND == kEncoderFused ? nullptr : tcond_row(a, l, s, a.Hkv * a.G * D);
   merge_partials<D, NW * 64>(pb, a, vec_off(0), KIND == kEncoderFused ? (int64_t)a.Hkv * D : D,
-                             (int)threadIdx.x);
+                             (int)threadIdx.x, tg ? tg + g * a.G * D : nullptr);
   if (threadIdx.x == 0)
     __hip_atomic_store(a.tickets + item, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -931,10 +983,20 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a) {
       if (j0 + u < ns) num += sm_f[j0 + u][h] * v[u];
   }
   const float den = sm_den[h];
-  const float o = den > 0.f ? num / den : 0.f;
+  float o = den > 0.f ? num / den : 0.f;
   int64_t off;
   if (KIND == kEncoderFused) off = ((((int64_t)l * a.S + s) * a.F + h) * a.Hkv + g) * D + d;
   else off = ((((int64_t)l * a.S + s) * a.Hkv + g) * a.G + h) * D + d;
+  if (KIND != kEncoderFused) {
+    // delay conditioning of the stored value
+    const int hidden = a.Hkv * a.G * D;
+    const float* tg = tcond_row(a, l, s, hidden);
+    if (tg) {
+      const int i = (g * a.G + h) * D + d;
+      const float x = a.out_f32 ? o : bf2f(f2bf(o));
+      o = fmaf(x, 1.0f + tg[i], tg[hidden + i]);
+    }
+  }
   if (a.out_f32) reinterpret_cast<float*>(a.out)[off] = o;
   else reinterpret_cast<uint16_t*>(a.out)[off] = (uint16_t)f2bf(o);
 }

@@ -46,8 +46,24 @@ struct AttnArgs {
   const char* pull;
   int64_t pull_bytes;
   int32_t pull_blocks;
+  // Decoder: delay conditioning applied to the output as it is stored, with
+  // exactly the arithmetic of rkv_tcond_modulate on the stored value:
+  // out <- out (1 + gamma) + beta, the vectors of condition tc_cond[s] of
+  // tc_mod [L][tc_conds][2][Hq d]; null: none.
+  const float* tc_mod;
+  const int32_t* tc_cond;
+  int32_t tc_conds;
   Theta adv_theta;
 };
+
+// Modulation vector (gamma; beta follows `hidden` floats later) of a stream's
+// condition for one layer, or null when the stream's condition is off.
+__device__ __forceinline__ const float* tcond_row(const AttnArgs& a, int l, int s, int hidden) {
+  if (!a.tc_mod) return nullptr;
+  const int c = a.tc_cond[s];
+  if (c < 0 || c >= a.tc_conds) return nullptr;
+  return a.tc_mod + ((int64_t)l * a.tc_conds + c) * 2 * hidden;
+}
 
 enum AttnKind { kDecodeRead = 0, kDecodeFused = 1, kEncoderFused = 2 };
 

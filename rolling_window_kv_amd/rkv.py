@@ -47,6 +47,7 @@ ENTRY_POINTS = (
     "rkv_mel_filters_host", "rkv_mel_step",
     "rkv_encoder_layer_weight_bytes", "rkv_encoder_step_workspace_bytes", "rkv_encoder_step",
     "rkv_tcond_delay_tokens", "rkv_tcond_prepare", "rkv_tcond_modulate",
+    "rkv_decode_step_pipelined_tcond",
 )
 
 RKV_TCOND_MAX_CONDS = 64
@@ -186,6 +187,9 @@ def lib():
                                   ctypes.c_int),
             "rkv_tcond_modulate": ([pc, ctypes.POINTER(rkv_tcond_cfg), vp, vp, vp, vp],
                                    ctypes.c_int),
+            "rkv_decode_step_pipelined_tcond": (
+                [pc, ctypes.POINTER(rkv_tcond_cfg), vp, vp, vp, vp, vp, pk, vp, vp, vp, vp, vp,
+                 sz, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -520,6 +524,19 @@ def rkv_decode_step_pipelined(cfg, state, plan, plan_next, kv, q, k_new, v_new, 
                                            _ptr(plan_next), ctypes.byref(kv), _ptr(q),
                                            _ptr(k_new), _ptr(v_new), _ptr(out), wp, wb,
                                            _stream(stream)))
+
+
+def rkv_decode_step_pipelined_tcond(cfg, tc, mod, stream_cond, state, plan, plan_next, kv, q,
+                                    k_new, v_new, out, workspace=None, stream=None):
+    """rkv_decode_step_pipelined with the delay conditioning of
+    rkv_tcond_modulate applied as the output is stored (same bits)."""
+    wp, wb = _ws(workspace)
+    _check("rkv_decode_step_pipelined_tcond",
+           lib().rkv_decode_step_pipelined_tcond(ctypes.byref(cfg), ctypes.byref(tc), _ptr(mod),
+                                                 _ptr(stream_cond), _ptr(state), _ptr(plan),
+                                                 _ptr(plan_next), ctypes.byref(kv), _ptr(q),
+                                                 _ptr(k_new), _ptr(v_new), _ptr(out), wp, wb,
+                                                 _stream(stream)))
 
 
 def rkv_encoder_chunk_attn(cfg, plan, kv, q, k_new, v_new, out, workspace=None, stream=None):

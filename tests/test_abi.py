@@ -426,6 +426,19 @@ def test_tcond_sizes_and_validation(rkv):
     narrow = rkv.make_tcond_cfg(L, 1024, dim=256, num_conds=C)
     assert mod(c, ctypes.byref(narrow), F, F, F) == rkv.RKV_EINVAL
     assert mod(N, t, F, F, F) == rkv.RKV_EINVAL
+    # the decode step with the modulation applied as it stores its output
+    kv = fake_view(rkv)
+    k = ctypes.byref(kv)
+    fused = lambda c_, t_, a, b: call(rkv, "rkv_decode_step_pipelined_tcond", c_, t_, a, b, F, F,
+                                      ctypes.c_void_p(FAKE + 0x100000), k, F, F, F, F, N, 0, N)
+    assert fused(c, t, F, N) == rkv.RKV_EINVAL                 # no stream conditions
+    assert fused(c, t, M, F) == rkv.RKV_EALIGN                 # misaligned vectors
+    assert fused(c, ctypes.byref(other), F, F) == rkv.RKV_EINVAL
+    assert fused(c, ctypes.byref(narrow), F, F) == rkv.RKV_EINVAL
+    assert fused(c, N, F, F) == rkv.RKV_EINVAL
+    enc = rkv.make_cfg(2, L, num_q_heads=16, num_kv_heads=16, head_dim=128,
+                       mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=4, max_cap=375)
+    assert fused(ctypes.byref(enc), t, F, F) == rkv.RKV_EINVAL  # decoder modes only
     assert rkv.rkv_last_hip_error() == 0
 
 

@@ -129,3 +129,64 @@ def test_full_size_decode_step_output():
             worst = max(worst, float(excess.max()))
     say(f"36 x 64 decode output modulated: worst |gpu - oracle| = {worst:.2f} bf16 ulp")
     assert worst <= 1.0
+
+
+FUSED_CASES = [
+    # name, mode, L, S, W, cap, splits, flags
+    ("rebase", "rebase", 3, 5, 40, 40, 0, 0),
+    ("rebase-f32", "rebase", 2, 5, 40, 40, 0, "f32"),
+    ("split-in-launch", "rebase", 2, 3, 120, 120, 3, 0),
+    ("split-merge-launch", "rebase", 2, 3, 120, 120, 3, "merge"),
+    ("split-f32", "rebase", 1, 3, 120, 120, 4, "f32"),
+    ("compact", "compact", 2, 3, 48, 64, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_step_equals_step_then_modulate(case):
+    """rkv_decode_step_pipelined_tcond against rkv_decode_step_pipelined +
+    rkv_tcond_modulate on identical caches: every output bit and every ring
+    byte the same, with streams on different conditions and some off (-1 and
+    an index past the last condition), unsplit and split key ranges."""
+    name, mode, L, S, W, cap, splits, flags = case
+    rkv = rkv_mod()
+    dev = device()
+    fl = {0: 0, "f32": rkv.RKV_F_OUT_F32, "merge": rkv.RKV_F_MERGE_LAUNCH}[flags]
+    md = rkv.RKV_MODE_REBASE if mode == "rebase" else rkv.RKV_MODE_COMPACT
+    cfg = rkv.make_cfg(S, L, mode=md, rebase_chunk=5, flags=fl, num_splits=splits)
+    hidden, C = 16 * 128, 4
+    tc = rkv.make_tcond_cfg(L, hidden, dim=64, num_conds=C, max_frame_len=8)
+    gen = torch.Generator().manual_seed(77)
+    mod = (0.2 * torch.randn((L, C, 2, hidden), generator=gen)).to(dev)
+    cond = torch.tensor([2, -1, 0, 3, C][:S], dtype=torch.int32, device=dev)
+    T, P = 70, 16
+    q = torch.randn((P, L, S, 16, 128), generator=gen).to(torch.bfloat16).to(dev)
+    k = torch.randn((P, L, S, 2, 128), generator=gen).to(torch.bfloat16).to(dev)
+    v = torch.randn((P, L, S, 2, 128), generator=gen).to(torch.bfloat16).to(dev)
+    odt = torch.float32 if flags == "f32" else torch.bfloat16
+    origins = np.arange(S, dtype=np.int64) * 7
+    caches = [rkv.Cache(cfg, cap, W, cap, origins, device=dev) for _ in range(2)]
+    outs = [torch.full((T, L, S, 16, 128), float("nan"), dtype=odt, device=dev) for _ in range(2)]
+    say(f"case {name}: L={L} S={S} W={W} cap={cap} splits={splits or 'auto'} flags={flags}")
+    for c in caches:
+        rkv.rkv_advance(cfg, c.state, c.plan)
+    for t in range(T):
+        j = t % P
+        for i, c in enumerate(caches):
+            cur, nxt = (c.plan, c.plan_next) if t % 2 == 0 else (c.plan_next, c.plan)
+            if md == rkv.RKV_MODE_COMPACT:
+                rkv.rkv_compact(cfg, cur, c.kv)
+            if i == 0:
+                rkv.rkv_decode_step_pipelined(cfg, c.state, cur, nxt, c.kv, q[j], k[j], v[j],
+                                              outs[0][t], c.workspace)
+                rkv.rkv_tcond_modulate(cfg, tc, mod, cond, outs[0][t])
+            else:
+                rkv.rkv_decode_step_pipelined_tcond(cfg, tc, mod, cond, c.state, cur, nxt, c.kv,
+                                                    q[j], k[j], v[j], outs[1][t], c.workspace)
+    torch.cuda.synchronize()
+    view = torch.int32 if odt == torch.float32 else torch.int16
+    same = outs[0].view(view) == outs[1].view(view)
+    say(f"  outputs identical: {int(same.sum())} of {same.numel()}")
+    assert bool(torch.isfinite(outs[1].float()).all())
+    assert bool(same.all())
+    assert torch.equal(caches[0].buf.view(torch.int16), caches[1].buf.view(torch.int16))
