@@ -13,7 +13,10 @@ import os
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librkv.so")
+# RKV_LIBRARY names another build of the same sources (the host-sanitizer
+# test loads an instrumented copy); by default the in-tree librkv.so.
+_LIB_PATH = os.environ.get("RKV_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "librkv.so")
 
 RKV_OK = 0
 RKV_EINVAL = -1
