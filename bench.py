@@ -947,7 +947,7 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: streams are independent, so N GPUs would each "
               "run the same per-GPU workload on their own streams with no communication; "
-              "multi-GPU runs are not part of this build.", file=sys.stderr)
+              "this benchmark measures the one-GPU share only.", file=sys.stderr)
         sys.exit(2)
     if args.mel:
         print(json.dumps(run_mel(args)), flush=True)
