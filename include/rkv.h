@@ -203,6 +203,18 @@ int rkv_state_init_host(const rkv_cfg* cfg, const int32_t* h_window,
                         const int32_t* h_cap, const int64_t* h_origin,
                         rkv_stream_state* h_state);
 
+/* Host: advance h_state[0..S) by `steps` steps in place, with exactly the
+ * state changes of `steps` rkv_advance calls (the step rules of the three
+ * modes: Audio8 explainer "Rolling KV Cache 三步拆解" steps 1-2, voxtral.c
+ * explainer sections 二 and 三), without writing plans or touching a device.
+ * For callers that resume streams at a known step without replaying the
+ * launches (rings filled by other means, checkpoints).  The states must be
+ * ones the rules can reach from rkv_state_init_host: window >= 1, 0 <= len <=
+ * cap <= cfg->max_cap, origin >= 0, t >= origin - 1 and the mode's capacity
+ * rule (RKV_ESTATE otherwise); steps >= 0 and max_cap >= 1 (RKV_EINVAL).  On
+ * an error no state is changed. */
+int rkv_state_advance_host(const rkv_cfg* cfg, rkv_stream_state* h_state, int64_t steps);
+
 /* The same initial states as rkv_state_init_host, written to d_state[0..S)
  * (device memory, 8-byte aligned) with copies on hip_stream.  Host arrays as
  * above.  Blocks until the copies are done (set-up, not the per-step path);

@@ -299,6 +299,34 @@ int rkv_state_init_host(const rkv_cfg* cfg, const int32_t* h_window, const int32
   return RKV_OK;
 }
 
+int rkv_state_advance_host(const rkv_cfg* cfg, rkv_stream_state* h_state, int64_t steps) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!h_state || steps < 0) return RKV_EINVAL;
+  if (cfg->max_cap < 1) return RKV_EINVAL;
+  for (int s = 0; s < cfg->num_streams; ++s) {
+    const rkv_stream_state& x = h_state[s];
+    if (x.window < 1 || x.cap < 1 || x.cap > cfg->max_cap || x.len < 0 || x.len > x.cap ||
+        x.origin < 0 || x.t < x.origin - 1)
+      return RKV_ESTATE;
+    switch (cfg->mode) {
+      case RKV_MODE_REBASE:
+        if (x.cap != x.window) return RKV_ESTATE;
+        break;
+      case RKV_MODE_COMPACT:
+        if (x.cap <= x.window) return RKV_ESTATE;
+        break;
+      default:
+        if (x.cap < x.window + cfg->new_rows) return RKV_ESTATE;
+        break;
+    }
+  }
+  for (int s = 0; s < cfg->num_streams; ++s)
+    for (int64_t i = 0; i < steps; ++i)
+      h_state[s] = rkv::make_plan(h_state[s], cfg->mode, cfg->rebase_chunk, cfg->new_rows).next;
+  return RKV_OK;
+}
+
 int rkv_state_init(const rkv_cfg* cfg, rkv_stream_state* d_state, const int32_t* h_window,
                    const int32_t* h_cap, const int64_t* h_origin, void* hip_stream) {
   int rc = check_cfg(cfg);

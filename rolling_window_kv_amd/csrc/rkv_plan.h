@@ -50,7 +50,10 @@ __host__ __device__ inline rkv_stream_state initial_state(int64_t origin, int32_
   return st;
 }
 
-__device__ inline PlanHead make_plan(const rkv_stream_state& x, int mode, int dc, int F) {
+// One step's plan header and the state after it (host and device: the host
+// uses it to advance states without launches).
+__host__ __device__ inline PlanHead make_plan(const rkv_stream_state& x, int mode, int dc,
+                                              int F) {
   PlanHead p;
   p.next = x;
   p.delta = 0;

@@ -43,7 +43,7 @@ RKV_NOALLOC_MAX_SPLIT_ITEMS = 16384
 # Entry points declared in include/rkv.h (checked by the ABI tests).
 ENTRY_POINTS = (
     "rkv_version", "rkv_strerror", "rkv_last_hip_error", "rkv_validate_cfg",
-    "rkv_state_init_host", "rkv_state_init", "rkv_workspace_bytes", "rkv_advance", "rkv_append",
+    "rkv_state_init_host", "rkv_state_advance_host", "rkv_state_init", "rkv_workspace_bytes", "rkv_advance", "rkv_append",
     "rkv_roll_rebase", "rkv_update_step", "rkv_compact", "rkv_decode_attn", "rkv_decode_step",
     "rkv_decode_step_noalloc", "rkv_decode_step_pipelined", "rkv_decode_attn_pipelined",
     "rkv_encoder_chunk_attn", "rkv_reset_streams", "rkv_restart_step",
@@ -159,6 +159,7 @@ def lib():
             "rkv_last_hip_error": ([], ctypes.c_int),
             "rkv_validate_cfg": ([pc], ctypes.c_int),
             "rkv_state_init_host": ([pc, vp, vp, vp, vp], ctypes.c_int),
+            "rkv_state_advance_host": ([pc, vp, ctypes.c_int64], ctypes.c_int),
             "rkv_state_init": ([pc, vp, vp, vp, vp, vp], ctypes.c_int),
             "rkv_workspace_bytes": ([pc, i32], sz),
             "rkv_advance": ([pc, vp, vp, vp], ctypes.c_int),
@@ -301,6 +302,17 @@ def rkv_state_init_host(cfg, window, cap, origin) -> np.ndarray:
                                    o.ctypes.data, out.ctypes.data)
     _check("rkv_state_init_host", rc)
     return out
+
+
+def rkv_state_advance_host(cfg, states, steps):
+    """Advance host states (a STATE_DTYPE array, e.g. from rkv_state_init_host)
+    by `steps` steps in place, as that many rkv_advance calls would."""
+    if states.dtype != STATE_DTYPE or not states.flags.c_contiguous or \
+            states.shape != (cfg.num_streams,):
+        raise ValueError("states must be a contiguous STATE_DTYPE array of num_streams entries")
+    _check("rkv_state_advance_host",
+           lib().rkv_state_advance_host(ctypes.byref(cfg), states.ctypes.data, int(steps)))
+    return states
 
 
 def rkv_reset_streams(cfg, state, plan, streams, origin, stream=None):

@@ -97,3 +97,34 @@ def test_device_state_init_equals_host_build():
     got = state.cpu().numpy()
     ref = rkv.rkv_state_init_host(cfg, windows, windows, origins).view(np.uint8)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("mode", ["rebase", "compact", "encoder"])
+def test_host_advance_equals_device_advance(mode):
+    """rkv_state_advance_host(n) leaves the same state bytes as n rkv_advance
+    launches (the bench starts its counter runs from such a state)."""
+    rkv = rkv_mod()
+    dev = device()
+    if mode == "rebase":
+        cfg = rkv.make_cfg(3, 1, rebase_chunk=25, max_cap=375)
+        w = c = np.array([375, 250, 188], np.int32)
+        steps = 437
+    elif mode == "compact":
+        cfg = rkv.make_cfg(3, 1, mode=rkv.RKV_MODE_COMPACT, max_cap=80)
+        w, c = np.array([64, 8, 5], np.int32), np.array([80, 12, 6], np.int32)
+        steps = 301
+    else:
+        cfg = rkv.make_cfg(2, 1, num_q_heads=20, num_kv_heads=20, head_dim=64,
+                           mode=rkv.RKV_MODE_ENC_CHUNK, new_rows=4, max_cap=754)
+        w, c = np.array([750, 30], np.int32), np.array([754, 34], np.int32)
+        steps = 200
+    o = np.arange(cfg.num_streams, dtype=np.int64) * 11
+    say(f"host advance vs device: mode={mode} steps={steps}")
+    host = rkv.rkv_state_init_host(cfg, w, c, o)
+    state = torch.from_numpy(host.view(np.uint8).copy()).to(dev)
+    plan = torch.zeros(cfg.num_streams * rkv.PLAN_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+    for _ in range(steps):
+        rkv.rkv_advance(cfg, state, plan)
+    torch.cuda.synchronize()
+    rkv.rkv_state_advance_host(cfg, host, steps)
+    assert np.array_equal(state.cpu().numpy(), host.view(np.uint8))
