@@ -216,7 +216,7 @@ __device__ __forceinline__ void merge_partials(__amdgpu_buffer_rsrc_t pb, const 
   }
 }
 
-template <int D, int NW, int KIND, bool COMP, typename SF>
+template <int D, int NW, int KIND, bool COMP, typename SF, bool KL>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(Occupancy<D, COMP>::waves)))
 void attn_kernel(AttnArgs args) {
@@ -359,8 +359,22 @@ void attn_kernel(AttnArgs args) {
   // partial tile reads valid data; its masked keys get probability 0.
   auto load_tile = [&](int key0, Tile& T, int lim) {
     const int rk = key0 + c < lim ? key0 + c : lim;
+    if (KL) {
+      // K in whole 128-byte lines, streamed: load st = 2 ln + h reads line ln
+      // of keys key0 + 8 h .. + 7, lane -> key lane & 7, 16-byte chunk
+      // 4 ((lane >> 3) & 1) + (lane >> 4) of the line; fix_k() moves the
+      // words to the operand layout before the tile is used
+      const int kr0 = key0 + (lane & 7);
+      const int ch = 4 * ((lane >> 3) & 1) + (lane >> 4);
 #pragma unroll
-    for (int st = 0; st < KS; ++st) T.k[st] = ld16(Kp + rk * rs + 32 * st + 8 * g4);
+      for (int st = 0; st < KS; ++st) {
+        const int r = kr0 + 8 * (st & 1) < lim ? kr0 + 8 * (st & 1) : lim;
+        T.k[st] = ld16_stream(Kp + r * rs + 64 * (st >> 1) + 8 * ch);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < KS; ++st) T.k[st] = ld16(Kp + rk * rs + 32 * st + 8 * g4);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rv0 = key0 + 4 * g4 + j;
@@ -629,6 +643,27 @@ void attn_kernel(AttnArgs args) {
 
   // reb: std::integral_constant<bool, re-base this launch's tiles>
   auto process = [&](Tile& T, int key0, auto reb) __attribute__((always_inline)) {
+    if (KL) {
+      // fix_k: from the line layout to the operand layout (key key0 + c,
+      // chunk 4 st + g4).  For line ln, operand st = 2 ln + s of lane m takes
+      // the word of load 2 ln + (bit 3 of m) from lane m with bit 3 set to s:
+      // the same lane, or its partner 8 lanes away (a row rotation by 8).
+      const bool hi = (lane & 8) != 0;
+#pragma unroll
+      for (int ln = 0; ln < KS / 2; ++ln) {
+        const u32x4 x0 = T.k[2 * ln], x1 = T.k[2 * ln + 1];
+        u32x4 r0, r1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t a1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x1[e], 0x128, 0xF, 0xF, false);
+          const uint32_t a0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x0[e], 0x128, 0xF, 0xF, false);
+          r0[e] = hi ? a1 : x0[e];
+          r1[e] = hi ? x1[e] : a0;
+        }
+        T.k[2 * ln] = r0;
+        T.k[2 * ln + 1] = r1;
+      }
+    }
     if (KIND == kDecodeFused && decltype(reb)::value && delta != 0) {
       __builtin_amdgcn_sched_barrier(0);
       // Exact re-base of the tile's rows in registers (R(-D), float32, rounded
@@ -1009,22 +1044,40 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnArgs a) {
 // resident 2-wave workgroups) is faster with 4, as is every d = 128 case.
 constexpr int64_t kManyItems = 12288;
 
-template <int D, int NW, int KIND, bool COMP, typename SF>
+template <int D, int NW, int KIND, bool COMP, typename SF, bool KL>
 hipError_t launch_nw(const AttnArgs& args, int items, hipStream_t stream) {
   const int extra = args.adv_state ? (args.S + NW - 1) / NW
                                     : (KIND == kEncoderFused && args.pull ? args.pull_blocks : 0);
-  hipLaunchKernelGGL((attn_kernel<D, NW, KIND, COMP, SF>),
+  hipLaunchKernelGGL((attn_kernel<D, NW, KIND, COMP, SF, KL>),
                      dim3(items * args.nsplit + extra), dim3(NW * 64), 0, stream, args);
   return hipGetLastError();
 }
 
+// Decoder launches whose workgroups stream at most this many rows read K as
+// whole lines with the non-temporal hint (the key-tile loads in the operand
+// layout touch half lines, which the hint makes slower).  Measured on the
+// same launches, same bits: 36 x 64 at W = 375 (375 rows) 157.4 -> 153.6 us,
+// 36 x 256 mixed windows pipelined 507 -> 497 us, 26 x 16 compaction at
+// W = 8192 split 24 ways (342 rows) 697 -> 682 us; but split 8 ways (1,024
+// rows) 581 -> 588 us and 3 ways (2,736 rows) 558 -> 568 us, and the d = 64
+// encoder chunks (754 rows) 2.64 -> 2.67 ms.
+constexpr int kLineRows = 512;
+
 template <int D, int KIND, bool COMP, typename SF>
 hipError_t launch_kind(const AttnArgs& args, int items, hipStream_t stream) {
   hipError_t e;
-  if (D == 64 && (int64_t)items * args.nsplit >= kManyItems)
-    e = launch_nw<D, 2, KIND, COMP, SF>(args, items, stream);
-  else
-    e = launch_nw<D, 4, KIND, COMP, SF>(args, items, stream);
+  const int per = (((args.ring.slots + args.nsplit - 1) / args.nsplit) + 15) & ~15;
+  if constexpr (D == 128 && KIND != kEncoderFused) {
+    if (per <= kLineRows)
+      e = launch_nw<D, 4, KIND, COMP, SF, true>(args, items, stream);
+    else
+      e = launch_nw<D, 4, KIND, COMP, SF, false>(args, items, stream);
+  } else {
+    if (D == 64 && (int64_t)items * args.nsplit >= kManyItems)
+      e = launch_nw<D, 2, KIND, COMP, SF, false>(args, items, stream);
+    else
+      e = launch_nw<D, 4, KIND, COMP, SF, false>(args, items, stream);
+  }
   if (e != hipSuccess || args.nsplit == 1 || args.tickets) return e;
   hipLaunchKernelGGL((combine_kernel<D, KIND>), dim3(items), dim3(kCombineThreads), 0, stream,
                      args);
