@@ -109,13 +109,16 @@ def test_split_key_ranges_agree(splits):
             check_close(f64(out)[:, l, s], sf, 1e-3, f"splits={splits} l{l} s{s}", ulp_slack=True)
 
 
+@pytest.mark.parametrize("W,cap", [(64, 80), (30, 31)])
 @pytest.mark.parametrize("fused", [True, False])
-def test_compaction_mode(fused):
-    """Logical-offset compaction: window 64, capacity 80, 300 steps (several
-    compactions), 2 layers x 2 streams."""
+def test_compaction_mode(fused, W, cap):
+    """Logical-offset compaction, 300 steps, 2 layers x 2 streams: window 64
+    in 80 rows (a compaction every 17 steps), and window 30 in 31 rows, where
+    every step once full drops one row and moves the other 30 down by one
+    (the most overlapped move)."""
     rkv = rkv_mod()
     dev = device()
-    L, S, T, W, cap = 2, 2, 300, 64, 80
+    L, S, T = 2, 2, 300
     origins = np.array([0, 4242], np.int64)
     q, k, v = _inputs(1005, L, S, T)
     cfg = rkv.make_cfg(S, L, mode=rkv.RKV_MODE_COMPACT)

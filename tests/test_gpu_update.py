@@ -124,7 +124,7 @@ def test_append_call_matches_oracle(mode, d, comp):
 
 
 @pytest.mark.parametrize("W,cap,d", [(64, 80, 128), (100, 250, 128), (40, 47, 64),
-                                     (8192, 9216, 128)])
+                                     (30, 31, 128), (8192, 9216, 128)])
 def test_compaction_move_is_exact(W, cap, d):
     rkv = rkv_mod()
     dev = device()
